@@ -1,0 +1,223 @@
+"""Benchmark: unique tokens/s of the tree conv + tree Gated DeltaNet forward.
+
+    python bench.py [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline]
+
+One step is one pass of the whole hot path over the resident synthetic batch:
+tree_conv over x [N, C] and tree_gdn_scan (one launch per trie level) over
+q, k, v, g, beta.  Inputs are generated on the GPU before timing; W untimed
+steps, then K timed steps between two synchronisations.  Kernel times come
+from HIP events recorded on the stream the kernels are launched on.
+
+Prints ONE JSON line (rank 0, one GPU).  The default workload is the large RL
+batch trie (32 prompts x 8 completions, a quarter of the completions forking
+into 2 continuations; N = 428,843 unique tokens; 16 query/key and 32 value
+heads of 128; bf16; conv over 8192 channels, width 4).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def scan_bytes_per_token(s):
+    """Algorithmic HBM bytes per token of the scan: read q, k (H_qk*d_k bf16
+    each), v (H_v*d_v), g and beta (H_v fp32 each); write o (H_v*d_v)."""
+    e = 2 if s.dtype == "bf16" else 4
+    return 2 * s.h_qk * s.d_k * e + 2 * s.h_v * s.d_v * e + 2 * s.h_v * 4
+
+
+def conv_bytes_per_token(s):
+    """Read x and write y, C channels each."""
+    e = 2 if s.dtype == "bf16" else 4
+    return 2 * s.channels * e
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gdn_scan.hip", "tree_conv.hip"):
+        with open(os.path.join(ROOT, "prefix_tree_packed_plan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """Measured HBM bytes per launch from the committed counter summary, or
+    None when the summary is missing or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(f"{kernel}:{workload}")
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """The oracle as it stands, on one core, over a bounded sample: the first
+    root-to-leaf path, conv over all channels and the recurrence over as many
+    value heads as fit the time budget.  Scaled to the whole job (every path,
+    every head), since the oracle's cost is linear in path tokens x heads."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import conv as oconv
+    from oracle import gdn as ogdn
+    from oracle import trie as otrie
+
+    s = wl.spec
+    t = wl.tensors
+    path = otrie.leaf_paths(wl.parents)[0]
+    idx = otrie.path_token_index(path, wl.seg_lens)
+    import torch
+    it = torch.as_tensor(idx, device=t["x"].device)
+    host = {k: v.index_select(0, it).double().cpu().numpy() for k, v in t.items() if k != "w"}
+    w = t["w"].double().cpu().numpy()
+    total_path = otrie.path_token_count(wl.parents, wl.seg_lens)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oconv.conv_on_path(host["x"], w)
+        t_conv = time.perf_counter() - t0
+        heads_done, t_scan = 0, 0.0
+        L = len(idx)
+        while heads_done < s.h_v and t_scan < budget_s:
+            t0 = time.perf_counter()
+            ogdn.gdn_on_path(host["q"], host["k"], host["v"], host["g"], host["beta"],
+                             heads=[heads_done])
+            t_scan += time.perf_counter() - t0
+            heads_done += 1
+    full_s = (t_conv + t_scan * s.h_v / heads_done) * total_path / L
+    return {
+        "value": wl.n_tokens / full_s,
+        "unit": "unique tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"first root-to-leaf path ({L} tokens of {total_path} path tokens): conv over all "
+                   f"{s.channels} channels and the token-by-token recurrence for {heads_done} of {s.h_v} "
+                   f"value heads, {t_conv + t_scan:.1f} s on 1 core; scaled linearly to every path and head"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the tree forward here is a single-GPU path "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import prefix_tree_packed_plan_amd as ptp
+    from workloads import make_workload
+
+    dev = "cuda:0"
+    wl = make_workload(args.config, dev)
+    s, t = wl.spec, wl.tensors
+    plan = ptp.tree_plan(wl.parents, wl.seg_lens, s.conv_width)
+    st = plan.stats
+    y = torch.empty_like(t["x"])
+    o = torch.empty_like(t["v"])
+    lib = ptp.load()
+    ws_bytes = int(lib.tree_scan_workspace_bytes(plan.handle, s.h_v, s.d_k, s.d_v, 0))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    plan.on_device(dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        ptp.tree_conv(t["x"], t["w"], plan, out=y)
+        if ev:
+            ev[1].record()
+        ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, out=o, workspace=ws)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    conv_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ms_per_step = 1e3 * wall / args.steps
+
+    n = wl.n_tokens
+    state_bytes = 2 * st["n_parents"] * s.h_v * s.d_k * s.d_v * 4  # write + read once
+    conv_b = n * conv_bytes_per_token(s)
+    scan_b = n * scan_bytes_per_token(s) + state_bytes
+    n_levels = st["n_levels"]
+    kernels = {
+        "tree_conv": {"ms": conv_ms, "bytes": conv_b, "launches": 1,
+                      "GB/s": conv_b / conv_ms / 1e6},
+        "tree_gdn_scan": {"ms": scan_ms, "bytes": scan_b, "launches": n_levels,
+                          "GB/s": scan_b / scan_ms / 1e6},
+    }
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    kd = kernels[dom]
+    achieved = kd["bytes"] / kd["launches"] / (kd["ms"] / kd["launches"] * 1e-3) / 1e9
+    traffic = load_traffic(dom, s.name)
+    out = {
+        "metric": "unique tokens/sec of tree conv+GDN forward",
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "unique tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{s.name}: {st['n_seg']} segments, {st['n_levels']} levels, {st['n_leaves']} leaves, "
+                         f"N={n} unique tokens ({st['path_tokens']} path tokens), heads {s.h_qk} qk / {s.h_v} v, "
+                         f"d_k=d_v={s.d_k}, conv C={s.channels} W={s.conv_width}"),
+            "n_unique_tokens": n,
+            "path_tokens": st["path_tokens"],
+            "work_saved_vs_rescan": st["path_tokens"] / n,
+            "por": st["por"],
+            "parallelism": "1 GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "kernels": kernels,
+        "roofline_combined_frac": ((conv_b + scan_b) / (HBM_PEAK_GBS * 1e9)) / ((conv_ms + scan_ms) * 1e-3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

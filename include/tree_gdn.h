@@ -1,0 +1,200 @@
+/*
+ * tree_gdn.h -- C ABI of the tree conv + tree Gated DeltaNet forward library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The library runs the forward pass of a recurrent mixer over a prefix trie
+ * whose segments are packed one after another (depth-first order, "Tree
+ * Training: Accelerating Agentic LLMs Training via Shared Prefix Reuse",
+ * arXiv 2511.00413, section 3.1 Eq. 8):
+ *
+ *   - tree_conv: a short causal depthwise conv1d in which every segment reads
+ *     the last W-1 inputs of its own root-to-segment path (same paper,
+ *     section 3.2 "Causal convolution", Eq. 11; tree-recurrence 0.1.0 project
+ *     page, "How a tree runs": the conv puts each segment's path history in
+ *     front of it in one call).
+ *   - tree_gdn_scan: a chunked gated delta rule in which every segment starts
+ *     from the final state of its parent segment and a root from zero (same
+ *     paper, section 3.2 "SSM Layers (GDN)", Eq. 10; appendix A.2), so
+ *     sibling branches never see each other's state.  Per value head, with
+ *     a_t = exp(g_t):
+ *         S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,
+ *         o_t = scale * S_t q_t.
+ *
+ * Every token's result equals the one a standalone forward over its own
+ * root-to-leaf path produces (same paper, section 3.1 Eq. 6).
+ *
+ * Conventions
+ *   - All functions return 0 (TREE_OK) or a negative TREE_ERR_* code; no
+ *     exception crosses the ABI.  tree_last_error() gives a message for the
+ *     last failure on the calling thread.
+ *   - Arguments are validated before any device work is enqueued; on failure
+ *     nothing is written.
+ *   - "device" pointers are HIP device memory owned by the caller.  The
+ *     library never allocates or frees device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All device
+ *     work is asynchronous and stream-ordered; buffers must stay alive until
+ *     the stream reaches the work.  Device faults surface at the caller's
+ *     next synchronisation.
+ *   - Tensors are packed token-major in segment order (token t of segment s
+ *     is row seg_off[s] + t).
+ */
+#ifndef TREE_GDN_H
+#define TREE_GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TREE_OK 0
+#define TREE_ERR_INVALID_ARG (-1) /* null pointer, bad enum, bad dimension      */
+#define TREE_ERR_BAD_TREE (-2)    /* parent not in [-1, i), length <= 0, n <= 0  */
+#define TREE_ERR_SIZE (-3)        /* n_tokens differs from the plan's token count */
+#define TREE_ERR_UNSUPPORTED (-4) /* head size / dtype / width not compiled in   */
+#define TREE_ERR_WORKSPACE (-5)   /* device plan or workspace too small          */
+#define TREE_ERR_HIP (-6)         /* a HIP runtime call failed                   */
+
+#define TREE_DTYPE_F32 0
+#define TREE_DTYPE_BF16 1
+
+#define TREE_ACT_NONE 0
+#define TREE_ACT_SILU 1
+
+#define TREE_SCHED_LEVEL 0 /* one launch per trie level; stream order is the barrier */
+
+typedef struct tree_plan tree_plan_t; /* opaque, host memory, immutable once built */
+
+typedef struct tree_plan_stats {
+  int64_t n_tokens;        /* N: sum of seg_lens (unique tokens)                       */
+  int64_t path_tokens;     /* sum over leaves of the root-to-leaf path length        */
+  int64_t max_path_tokens; /* longest root-to-leaf path                               */
+  double por;              /* potential overlap ratio 1 - N / path_tokens ("Tree
+                              Training" section 4.1, Eq. 12)                          */
+  int32_t n_seg;
+  int32_t n_roots;
+  int32_t n_leaves;
+  int32_t n_parents; /* segments with at least one child (they own a state slot) */
+  int32_t n_levels;  /* 1 + the largest depth                                    */
+  int32_t conv_width;
+} tree_plan_stats_t;
+
+/*
+ * tree_plan -- build the host plan of a trie (host only, no device work).
+ *
+ * parents[i]  parent segment of segment i, or -1 for a root; must lie in
+ *             [-1, i) (any topological numbering; depth-first pre-order is
+ *             the packed layout of "Tree Training" Eq. 8).  Several roots (a
+ *             forest) are allowed.
+ * seg_lens[i] tokens of segment i, >= 1.  Sum must be < 2^31.
+ * n_seg       number of segments, >= 1.
+ * conv_width  W of the causal conv, 1..8.
+ * out         receives a library-owned plan; free it with tree_plan_free.
+ *
+ * The plan holds: segment offsets; depths and the per-level segment order
+ * (longest segment first within a level); the state slot of every segment
+ * with children; and the conv history table hist[s][0..W-2], the packed row
+ * indices of the W-1 inputs preceding segment s on its path (-1 = zero pad):
+ * the last W-1 entries of hist[parent] followed by the parent's own rows.
+ * Inputs are copied; the plan is immutable and may be shared across threads.
+ */
+int tree_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
+              int32_t conv_width, tree_plan_t** out);
+
+/* Free a plan (NULL is a no-op).  Stream work that uses a device copy of the
+ * plan does not need the host plan to stay alive. */
+void tree_plan_free(tree_plan_t* plan);
+
+/* Copy the plan's statistics into *out. */
+int tree_plan_query(const tree_plan_t* plan, tree_plan_stats_t* out);
+
+/* Copy the conv history table (n_seg * (W-1) int32, row-major) into hist. */
+int tree_plan_conv_history(const tree_plan_t* plan, int32_t* hist);
+
+/* Copy the level schedule: level_start[0..n_levels] (int32) and
+ * order[0..n_seg-1] (segments of level L are order[level_start[L] ..
+ * level_start[L+1]-1], longest first, ties by index). */
+int tree_plan_levels(const tree_plan_t* plan, int32_t* level_start, int32_t* order);
+
+/* Bytes of device memory tree_plan_upload writes (the device copy of the plan). */
+size_t tree_plan_device_bytes(const tree_plan_t* plan);
+
+/*
+ * tree_plan_upload -- copy the plan into caller-owned device memory `dplan`
+ * (dplan_bytes >= tree_plan_device_bytes) with an asynchronous host-to-device
+ * copy on `stream`.  Do it once per plan; every tree_conv / tree_gdn_scan that
+ * names this plan then takes the same `dplan` (e.g. every layer of a forward).
+ * The source is the plan's own pageable host buffer, so the plan must stay
+ * alive until the copy has run (synchronise `stream` before freeing it).
+ */
+int tree_plan_upload(const tree_plan_t* plan, void* dplan, size_t dplan_bytes, void* stream);
+
+/*
+ * tree_conv -- tree-aware causal depthwise conv1d ("Tree Training" section
+ * 3.2 Eq. 11; the per-path definition of section 3.1 Eq. 6):
+ *
+ *   y[t, c] = act( sum_{i=0}^{W-1} w[c, i] * xin(t, i - (W-1), c) + bias[c] )
+ *
+ * where xin(t, -j, c) is the input j steps back along t's root path (zero
+ * before the root); w[c, W-1] multiplies token t itself.
+ *
+ * x     device, [n_tokens, channels], dtype           (read)
+ * w     device, [channels, W], dtype                  (read)
+ * bias  device, [channels], dtype, or NULL            (read)
+ * y     device, [n_tokens, channels], dtype           (written; must not alias x)
+ * dtype TREE_DTYPE_F32 or TREE_DTYPE_BF16; arithmetic in fp32.
+ * act   TREE_ACT_NONE or TREE_ACT_SILU (y = z * sigmoid(z)).
+ * dplan device copy of `plan` made by tree_plan_upload.
+ * Errors: INVALID_ARG, SIZE (n_tokens != plan N), UNSUPPORTED (W > 4),
+ * HIP.
+ */
+int tree_conv(const void* x, const void* w, const void* bias, void* y, int64_t n_tokens,
+              int32_t channels, int32_t dtype, int32_t act, const tree_plan_t* plan,
+              const void* dplan, void* stream);
+
+/*
+ * tree_scan_workspace_bytes -- device workspace tree_gdn_scan needs: one fp32
+ * state [h_v, d_k, d_v] per segment with children (0 when the caller passes
+ * `states`, which then carries the parent states).
+ */
+size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d_k, int32_t d_v,
+                                 int32_t with_states);
+
+/*
+ * tree_gdn_scan -- chunked gated delta rule over the trie ("Tree Training"
+ * section 3.2 Eq. 10 and appendix A.2; the recurrence at the top of this file).
+ *
+ * q, k   device, [n_tokens, h_qk, d_k], dtype          (read)
+ * v      device, [n_tokens, h_v, d_v], dtype           (read)
+ * g      device, [n_tokens, h_v], fp32: log decay, a_t = exp(g_t); g <= 0
+ *        keeps every exponent the kernel forms non-positive       (read)
+ * beta   device, [n_tokens, h_v], fp32                 (read)
+ * o      device, [n_tokens, h_v, d_v], dtype           (written)
+ * states device, [n_seg, h_v, d_k, d_v] fp32, or NULL: every segment's
+ *        state after its last token, [d_k, d_v] orientation (the appendix's
+ *        state tensor).  When given, children read their parents' states
+ *        from it and the workspace may be empty.         (written)
+ * Value head h uses query/key head h / (h_v / h_qk).
+ * scale  multiplies q (1.0 = the plain recurrence).
+ * dtype  TREE_DTYPE_BF16 (bf16 MFMA, fp32 accumulation, compensated
+ *        split-bf16 on the state path) or TREE_DTYPE_F32 (inputs split into
+ *        two bf16 parts on every product).
+ * sched  TREE_SCHED_LEVEL.
+ * ws     device workspace of ws_bytes >= tree_scan_workspace_bytes.
+ * Compiled head sizes: d_k = d_v in {32, 128} for bf16, 32 for fp32.
+ * Errors: INVALID_ARG, SIZE, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g,
+                  const float* beta, void* o, float* states, int64_t n_tokens, int32_t h_qk,
+                  int32_t h_v, int32_t d_k, int32_t d_v, float scale, int32_t dtype,
+                  int32_t sched, const tree_plan_t* plan, const void* dplan, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* tree_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREE_GDN_H */

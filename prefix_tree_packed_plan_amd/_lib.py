@@ -1,0 +1,258 @@
+"""ctypes binding of libtreegdn.so (include/tree_gdn.h).
+
+Argument marshalling only: PyTorch provides device memory and the current
+HIP stream; every step of the forward runs in the library's kernels.  There
+is no fallback: if the library is missing or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtreegdn.so")
+
+TREE_OK = 0
+ERRORS = {
+    -1: "TREE_ERR_INVALID_ARG",
+    -2: "TREE_ERR_BAD_TREE",
+    -3: "TREE_ERR_SIZE",
+    -4: "TREE_ERR_UNSUPPORTED",
+    -5: "TREE_ERR_WORKSPACE",
+    -6: "TREE_ERR_HIP",
+}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+ACT_NONE, ACT_SILU = 0, 1
+SCHED_LEVEL = 0
+
+# Every function the header declares, with its ctypes signature.
+_P, _I32, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+
+
+class PlanStats(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("path_tokens", ctypes.c_int64),
+        ("max_path_tokens", ctypes.c_int64),
+        ("por", ctypes.c_double),
+        ("n_seg", ctypes.c_int32),
+        ("n_roots", ctypes.c_int32),
+        ("n_leaves", ctypes.c_int32),
+        ("n_parents", ctypes.c_int32),
+        ("n_levels", ctypes.c_int32),
+        ("conv_width", ctypes.c_int32),
+    ]
+
+
+SIGNATURES = {
+    "tree_plan": (ctypes.c_int, [_P, _P, _I32, _I32, ctypes.POINTER(_P)]),
+    "tree_plan_free": (None, [_P]),
+    "tree_plan_query": (ctypes.c_int, [_P, ctypes.POINTER(PlanStats)]),
+    "tree_plan_conv_history": (ctypes.c_int, [_P, _P]),
+    "tree_plan_levels": (ctypes.c_int, [_P, _P, _P]),
+    "tree_plan_device_bytes": (_SZ, [_P]),
+    "tree_plan_upload": (ctypes.c_int, [_P, _P, _SZ, _P]),
+    "tree_conv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]),
+    "tree_scan_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
+    "tree_gdn_scan": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
+                                     _F, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "tree_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def load():
+    """Load the library (once).  Raises OSError if it has not been built."""
+    global _lib
+    if _lib is None:
+        # torch bundles its own HIP runtime under the same soname
+        # (libamdhip64.so.7).  Loading torch first makes the library's
+        # dependency bind to that runtime, so torch's tensors, streams and
+        # the kernels here share one HIP runtime and one device context.
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m prefix_tree_packed_plan_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+class TreeError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def _check(rc):
+    if rc != TREE_OK:
+        raise TreeError(rc, load().tree_last_error().decode())
+
+
+# --------------------------------------------------------------------- plan
+
+class TreePlan:
+    """Host plan of a packed trie (tree_plan), plus its device copies."""
+
+    def __init__(self, parents, seg_lens, conv_width: int = 4):
+        lib = load()
+        self._parents = np.ascontiguousarray(parents, dtype=np.int32)
+        self._lens = np.ascontiguousarray(seg_lens, dtype=np.int32)
+        if self._parents.shape != self._lens.shape or self._parents.ndim != 1:
+            raise ValueError("parents and seg_lens must be 1-D and of equal length")
+        h = _P()
+        _check(lib.tree_plan(self._parents.ctypes.data, self._lens.ctypes.data,
+                             int(self._parents.shape[0]), int(conv_width), ctypes.byref(h)))
+        self._h = h
+        st = PlanStats()
+        _check(lib.tree_plan_query(self._h, ctypes.byref(st)))
+        self.stats = {f: getattr(st, f) for f, _ in PlanStats._fields_}
+        self._dev = {}
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.stats["n_tokens"])
+
+    @property
+    def n_seg(self) -> int:
+        return int(self.stats["n_seg"])
+
+    @property
+    def conv_width(self) -> int:
+        return int(self.stats["conv_width"])
+
+    def conv_history(self) -> np.ndarray:
+        w1 = self.conv_width - 1
+        out = np.zeros((self.n_seg, max(w1, 0)), np.int32)
+        if w1 > 0:
+            _check(load().tree_plan_conv_history(self._h, out.ctypes.data))
+        return out
+
+    def levels(self):
+        ls = np.zeros(self.stats["n_levels"] + 1, np.int32)
+        order = np.zeros(self.n_seg, np.int32)
+        _check(load().tree_plan_levels(self._h, ls.ctypes.data, order.ctypes.data))
+        return ls, order
+
+    def device_bytes(self) -> int:
+        return int(load().tree_plan_device_bytes(self._h))
+
+    def on_device(self, device):
+        """The plan's device copy on `device` (uploaded once, stream-ordered)."""
+        import torch
+        dev = torch.device(device)
+        key = dev.index if dev.index is not None else torch.cuda.current_device()
+        if key not in self._dev:
+            buf = torch.empty(self.device_bytes(), dtype=torch.uint8, device=dev)
+            stream = torch.cuda.current_stream(buf.device).cuda_stream
+            _check(load().tree_plan_upload(self._h, buf.data_ptr(), buf.numel(), stream))
+            torch.cuda.current_stream(buf.device).synchronize()
+            self._dev[key] = buf
+        return self._dev[key]
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.tree_plan_free(h)
+            self._h = None
+
+
+def tree_plan(parents, seg_lens, conv_width: int = 4) -> TreePlan:
+    return TreePlan(parents, seg_lens, conv_width)
+
+
+# ------------------------------------------------------------------ kernels
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, name, dtype=None, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def tree_conv(x, w, plan: TreePlan, bias=None, act: Optional[str] = None, out=None):
+    """y = tree-aware causal depthwise conv of x [N, C] with w [C, W]."""
+    import torch
+    _need(x, "x")
+    _need(w, "w", x.dtype, x.device)
+    if bias is not None:
+        _need(bias, "bias", x.dtype, x.device)
+    if x.dim() != 2 or w.dim() != 2 or w.shape[0] != x.shape[1] or w.shape[1] != plan.conv_width:
+        raise ValueError("shapes must be x [N, C], w [C, W] with W = plan conv width")
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", x.dtype, x.device)
+    a = {None: ACT_NONE, "none": ACT_NONE, "silu": ACT_SILU, "swish": ACT_SILU}[act]
+    dplan = plan.on_device(x.device)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _check(load().tree_conv(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
+                            y.data_ptr(), x.shape[0], x.shape[1], _dtype_code(x), a, plan.handle,
+                            dplan.data_ptr(), stream))
+    return y
+
+
+def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_states: bool = False,
+                  out=None, states=None, workspace=None):
+    """Tree gated delta rule: o [N, H_v, d_v] (and states [n_seg, H_v, d_k, d_v] fp32)."""
+    import torch
+    _need(q, "q")
+    dev = q.device
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
+        raise ValueError("shapes must be q, k [N, H_qk, d_k] and v [N, H_v, d_v]")
+    n, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    if g.shape != (n, h_v) or beta.shape != (n, h_v):
+        raise ValueError("g and beta must be [N, H_v]")
+    o = torch.empty_like(v) if out is None else out
+    _need(o, "out", q.dtype, dev)
+    if return_states and states is None:
+        states = torch.empty((plan.n_seg, h_v, d_k, d_v), dtype=torch.float32, device=dev)
+    if states is not None:
+        _need(states, "states", torch.float32, dev)
+    lib = load()
+    need = int(lib.tree_scan_workspace_bytes(plan.handle, h_v, d_k, d_v, int(states is not None)))
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    dplan = plan.on_device(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib.tree_gdn_scan(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                             o.data_ptr(), states.data_ptr() if states is not None else None,
+                             n, h_qk, h_v, d_k, d_v, float(scale), _dtype_code(q), SCHED_LEVEL,
+                             plan.handle, dplan.data_ptr(),
+                             workspace.data_ptr() if workspace is not None else None,
+                             workspace.numel() if workspace is not None else 0, stream))
+    if return_states:
+        return o, states
+    return o

@@ -1,0 +1,183 @@
+// C ABI (include/tree_gdn.h): argument checks, the device plan, launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "../../include/tree_gdn.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+struct tree_plan {
+  tg::Plan p;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* f, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, f);
+  std::vsnprintf(buf, sizeof(buf), f, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(const char* what, hipError_t e) {
+  return fail(TREE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int32_t d) { return d == TREE_DTYPE_F32 || d == TREE_DTYPE_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+int tree_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg, int32_t conv_width,
+              tree_plan_t** out) {
+  if (!out) return fail(TREE_ERR_INVALID_ARG, "tree_plan: out is null");
+  *out = nullptr;
+  tree_plan_t* plan = new (std::nothrow) tree_plan_t;
+  if (!plan) return fail(TREE_ERR_INVALID_ARG, "tree_plan: out of host memory");
+  std::string err;
+  const int rc = tg::build_plan(parents, seg_lens, n_seg, conv_width, &plan->p, &err);
+  if (rc != TREE_OK) {
+    delete plan;
+    g_err = err;
+    return rc;
+  }
+  *out = plan;
+  return TREE_OK;
+}
+
+void tree_plan_free(tree_plan_t* plan) { delete plan; }
+
+int tree_plan_query(const tree_plan_t* plan, tree_plan_stats_t* out) {
+  if (!plan || !out) return fail(TREE_ERR_INVALID_ARG, "tree_plan_query: null argument");
+  const tg::Plan& p = plan->p;
+  out->n_tokens = p.n_tokens;
+  out->path_tokens = p.path_tokens;
+  out->max_path_tokens = p.max_path_tokens;
+  out->por = p.path_tokens > 0 ? 1.0 - static_cast<double>(p.n_tokens) / p.path_tokens : 0.0;
+  out->n_seg = p.n_seg;
+  out->n_roots = p.n_roots;
+  out->n_leaves = p.n_leaves;
+  out->n_parents = p.n_parents;
+  out->n_levels = p.n_levels;
+  out->conv_width = p.width;
+  return TREE_OK;
+}
+
+int tree_plan_conv_history(const tree_plan_t* plan, int32_t* hist) {
+  if (!plan || !hist) return fail(TREE_ERR_INVALID_ARG, "tree_plan_conv_history: null argument");
+  std::copy(plan->p.hist.begin(), plan->p.hist.end(), hist);
+  return TREE_OK;
+}
+
+int tree_plan_levels(const tree_plan_t* plan, int32_t* level_start, int32_t* order) {
+  if (!plan || !level_start || !order)
+    return fail(TREE_ERR_INVALID_ARG, "tree_plan_levels: null argument");
+  std::copy(plan->p.level_start.begin(), plan->p.level_start.end(), level_start);
+  std::copy(plan->p.order.begin(), plan->p.order.end(), order);
+  return TREE_OK;
+}
+
+size_t tree_plan_device_bytes(const tree_plan_t* plan) { return plan ? plan->p.device_bytes() : 0; }
+
+int tree_plan_upload(const tree_plan_t* plan, void* dplan, size_t dplan_bytes, void* stream) {
+  if (!plan || !dplan) return fail(TREE_ERR_INVALID_ARG, "tree_plan_upload: null argument");
+  if (dplan_bytes < plan->p.device_bytes())
+    return fail(TREE_ERR_WORKSPACE, "tree_plan_upload: dplan has %zu bytes, needs %zu", dplan_bytes,
+                plan->p.device_bytes());
+  const hipError_t e = hipMemcpyAsync(dplan, plan->p.mirror.data(), plan->p.device_bytes(),
+                                      hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("tree_plan_upload: hipMemcpyAsync", e);
+  return TREE_OK;
+}
+
+int tree_conv(const void* x, const void* w, const void* bias, void* y, int64_t n_tokens,
+              int32_t channels, int32_t dtype, int32_t act, const tree_plan_t* plan,
+              const void* dplan, void* stream) {
+  if (!plan || !x || !w || !y || !dplan) return fail(TREE_ERR_INVALID_ARG, "tree_conv: null argument");
+  const tg::Plan& p = plan->p;
+  if (n_tokens != p.n_tokens)
+    return fail(TREE_ERR_SIZE, "tree_conv: n_tokens %lld != plan tokens %lld",
+                static_cast<long long>(n_tokens), static_cast<long long>(p.n_tokens));
+  if (channels <= 0) return fail(TREE_ERR_INVALID_ARG, "tree_conv: channels must be > 0");
+  if (!dtype_ok(dtype)) return fail(TREE_ERR_INVALID_ARG, "tree_conv: bad dtype %d", dtype);
+  if (act != TREE_ACT_NONE && act != TREE_ACT_SILU)
+    return fail(TREE_ERR_INVALID_ARG, "tree_conv: bad activation %d", act);
+  if (p.width > 4) return fail(TREE_ERR_UNSUPPORTED, "tree_conv: conv width %d > 4", p.width);
+  if (x == y) return fail(TREE_ERR_INVALID_ARG, "tree_conv: y must not alias x");
+  const int32_t* base = static_cast<const int32_t*>(dplan);
+  tg::ConvArgs a{x, w, bias, y, static_cast<int32_t>(n_tokens), channels, p.width, dtype, act,
+                 base + p.m_seg_off, base + p.m_hist, p.n_seg};
+  const hipError_t e = tg::launch_conv(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("tree_conv: launch", e);
+  return TREE_OK;
+}
+
+size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d_k, int32_t d_v,
+                                 int32_t with_states) {
+  if (!plan || h_v <= 0 || d_k <= 0 || d_v <= 0 || with_states) return 0;
+  return static_cast<size_t>(plan->p.n_parents) * h_v * d_k * d_v * sizeof(float);
+}
+
+int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  void* o, float* states, int64_t n_tokens, int32_t h_qk, int32_t h_v, int32_t d_k,
+                  int32_t d_v, float scale, int32_t dtype, int32_t sched, const tree_plan_t* plan,
+                  const void* dplan, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !q || !k || !v || !g || !beta || !o || !dplan)
+    return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: null argument");
+  const tg::Plan& p = plan->p;
+  if (n_tokens != p.n_tokens)
+    return fail(TREE_ERR_SIZE, "tree_gdn_scan: n_tokens %lld != plan tokens %lld",
+                static_cast<long long>(n_tokens), static_cast<long long>(p.n_tokens));
+  if (h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0)
+    return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: head counts and sizes must be > 0");
+  if (h_v % h_qk != 0)
+    return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan: h_v %d is not a multiple of h_qk %d", h_v, h_qk);
+  if (!dtype_ok(dtype)) return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: bad dtype %d", dtype);
+  if (sched != TREE_SCHED_LEVEL) return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: bad schedule %d", sched);
+  if (!tg::scan_supported(d_k, d_v, dtype))
+    return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan: d_k=%d d_v=%d dtype=%d not compiled in", d_k,
+                d_v, dtype);
+  const size_t need = tree_scan_workspace_bytes(plan, h_v, d_k, d_v, states != nullptr);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(TREE_ERR_WORKSPACE, "tree_gdn_scan: workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0,
+                need);
+  const int32_t* base = static_cast<const int32_t*>(dplan);
+  tg::ScanArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.states = states;
+  a.slots = static_cast<float*>(ws);
+  a.seg_off = base + p.m_seg_off;
+  a.parent = base + p.m_parent;
+  a.slot = base + p.m_slot;
+  a.h_qk = h_qk;
+  a.h_v = h_v;
+  a.scale = scale;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int32_t l = 0; l < p.n_levels; ++l) {
+    a.items = base + p.m_order + p.level_start[l];
+    a.n_items = p.level_start[l + 1] - p.level_start[l];
+    const hipError_t e = tg::launch_scan_level(a, d_k, d_v, dtype, st);
+    if (e != hipSuccess) return hip_fail("tree_gdn_scan: launch", e);
+  }
+  return TREE_OK;
+}
+
+const char* tree_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

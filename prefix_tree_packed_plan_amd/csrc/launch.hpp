@@ -1,0 +1,54 @@
+// Internal kernel launchers shared by api.cpp and the .hip files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace tg {
+
+struct ConvArgs {
+  const void* x;
+  const void* w;
+  const void* bias;  // may be null
+  void* y;
+  int32_t n_tok;
+  int32_t channels;
+  int32_t width;  // 1..4
+  int32_t dtype;  // TREE_DTYPE_*
+  int32_t act;    // TREE_ACT_*
+  const int32_t* seg_off;  // device, n_seg + 1
+  const int32_t* hist;     // device, n_seg * (width - 1)
+  int32_t n_seg;
+};
+
+// Returns hipSuccess or the launch error.
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
+
+struct ScanArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  void* o;
+  float* states;  // [n_seg, h_v, d_k, d_v] or null
+  float* slots;   // [n_parents, h_v, d_k, d_v] when states is null
+  const int32_t* seg_off;
+  const int32_t* parent;
+  const int32_t* slot;
+  const int32_t* items;  // segments of this launch
+  int32_t n_items;
+  int32_t h_qk;
+  int32_t h_v;
+  float scale;
+};
+
+// One launch over `n_items` segments x h_v value heads.  Returns
+// hipErrorInvalidValue for a head size that is not compiled in.
+hipError_t launch_scan_level(const ScanArgs& a, int d_k, int d_v, int dtype, hipStream_t stream);
+
+// Whether (d_k, d_v, dtype) has a compiled scan kernel.
+bool scan_supported(int d_k, int d_v, int dtype);
+
+}  // namespace tg

@@ -1,0 +1,41 @@
+// Host-side trie plan (no HIP headers: this file and plan.cpp build and run
+// without a GPU).
+//
+// The plan is what "TreePlan is built once per forward on the host" means on
+// the tree-recurrence 0.1.0 project page ("How a tree runs"): segment
+// offsets, the level schedule that lets every segment start from its
+// parent's final state ("Tree Training" section 3.2, Eq. 10: parents precede
+// children), and the conv history table that gives each segment the last
+// W-1 inputs of its own path (section 3.2, Eq. 11).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace tg {
+
+struct Plan {
+  int32_t n_seg = 0;
+  int32_t width = 0;  // conv width W
+  int64_t n_tokens = 0;
+  int32_t n_roots = 0, n_leaves = 0, n_parents = 0, n_levels = 0;
+  int64_t path_tokens = 0, max_path_tokens = 0;
+
+  std::vector<int32_t> parents, lens, seg_off, depth, slot, hist;
+  std::vector<int32_t> level_start;  // n_levels + 1
+  std::vector<int32_t> order;        // segments by (level, length desc, index)
+
+  // Device copy: one int32 array; element offsets of each table inside it.
+  std::vector<int32_t> mirror;
+  size_t m_seg_off = 0, m_parent = 0, m_slot = 0, m_hist = 0, m_order = 0;
+
+  size_t device_bytes() const { return mirror.size() * sizeof(int32_t); }
+};
+
+// Returns 0 or a negative TREE_ERR_* code; on failure *err holds a message.
+int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
+               int32_t conv_width, Plan* out, std::string* err);
+
+}  // namespace tg

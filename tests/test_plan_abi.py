@@ -1,0 +1,159 @@
+"""Host plan and C-ABI checks that need no GPU.
+
+tree_plan is host-only, so the real library is called here; nothing in this
+file launches a kernel.  Expected values come from independent walks over the
+parent array written in this file or from the oracle's trie helpers.
+"""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import trie as otrie
+from oracle.brute import _prev_token_fn
+from prefix_tree_packed_plan_amd import _lib
+from workloads import CONFIGS, make_trie
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_gdn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tree_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_header_symbol():
+    lib = _lib.load()
+    names = header_functions()
+    assert "tree_plan" in names and "tree_gdn_scan" in names and "tree_conv" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def rand_trie(rng, n_seg, max_len, n_roots=1):
+    parents = [-1] * n_roots + [int(rng.integers(0, i)) for i in range(n_roots, n_seg)]
+    return np.array(parents, np.int32), rng.integers(1, max_len + 1, n_seg).astype(np.int32)
+
+
+@pytest.mark.parametrize("cid", sorted(CONFIGS))
+def test_plan_stats_match_the_trie(cid):
+    parents, lens, _ = make_trie(cid)
+    plan = _lib.TreePlan(parents, lens, 4)
+    st = plan.stats
+    leaves = otrie.leaves_of(parents)
+    assert st["n_tokens"] == int(lens.sum())
+    assert st["n_seg"] == len(parents)
+    assert st["n_leaves"] == len(leaves)
+    assert st["n_roots"] == int((parents < 0).sum())
+    assert st["n_parents"] == len(parents) - len(leaves)
+    assert st["path_tokens"] == otrie.path_token_count(parents, lens)
+    assert st["max_path_tokens"] == max(sum(int(lens[s]) for s in p) for p in otrie.leaf_paths(parents))
+    assert abs(st["por"] - otrie.por(parents, lens)) < 1e-12
+
+
+def test_plan_por_printed_example():
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "por_example.json")))
+    plan = _lib.TreePlan([-1, 0, 0], [81000, 1000, 1000], 4)
+    assert plan.stats["n_tokens"] == gold["n_tree"]
+    assert plan.stats["path_tokens"] == gold["n_base"]
+    assert round(100 * plan.stats["por"], 1) == gold["por_percent_rounded"]
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_conv_history_is_the_path_history(W, seed):
+    """hist[s][W-2-j] must be the packed row j+1 steps before segment s's first
+    token along its path (walked token by token), -1 before the root."""
+    rng = np.random.default_rng(seed)
+    parents, lens = rand_trie(rng, 50, 4, n_roots=3)
+    plan = _lib.TreePlan(parents, lens, W)
+    hist = plan.conv_history()
+    prev, _, start = _prev_token_fn(parents, lens)
+    for s in range(len(parents)):
+        j = start[s]
+        for back in range(1, W):
+            j = None if j is None else prev(j)
+            assert hist[s, W - 1 - back] == (-1 if j is None else j), (s, back)
+
+
+def test_levels_respect_depth_and_longest_first():
+    rng = np.random.default_rng(4)
+    parents, lens = rand_trie(rng, 80, 50, n_roots=2)
+    plan = _lib.TreePlan(parents, lens, 4)
+    ls, order = plan.levels()
+    depth = np.zeros(len(parents), int)
+    for i, p in enumerate(parents):
+        depth[i] = 0 if p < 0 else depth[p] + 1
+    assert sorted(order.tolist()) == list(range(len(parents)))
+    assert ls[0] == 0 and ls[-1] == len(parents) and len(ls) == depth.max() + 2
+    for lvl in range(len(ls) - 1):
+        segs = order[ls[lvl]:ls[lvl + 1]]
+        assert np.all(depth[segs] == lvl)
+        assert np.all(np.diff(lens[segs]) <= 0)
+
+
+@pytest.mark.parametrize("parents,lens,code", [
+    ([-1, 1], [3, 3], -2),        # self parent
+    ([-1, 2, 0], [3, 3, 3], -2),  # parent after child
+    ([-1, 0], [3, 0], -2),        # empty segment
+    ([-2], [3], -2),              # parent below -1
+])
+def test_bad_trees_are_rejected(parents, lens, code):
+    with pytest.raises(_lib.TreeError) as ei:
+        _lib.TreePlan(parents, lens, 4)
+    assert ei.value.code == code
+
+
+def test_argument_errors_need_no_device():
+    lib = _lib.load()
+    h = ctypes.c_void_p()
+    p = np.array([-1], np.int32)
+    n = np.array([5], np.int32)
+    assert lib.tree_plan(p.ctypes.data, n.ctypes.data, 0, 4, ctypes.byref(h)) == -2
+    assert lib.tree_plan(p.ctypes.data, n.ctypes.data, 1, 9, ctypes.byref(h)) == -1
+    assert lib.tree_plan(None, n.ctypes.data, 1, 4, ctypes.byref(h)) == -1
+    plan = _lib.TreePlan(p, n, 4)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    # token count mismatch
+    assert lib.tree_conv(fake, fake, None, fake, 6, 8, 1, 0, plan.handle, fake, None) == -3
+    # bad activation / dtype
+    assert lib.tree_conv(fake, fake, None, fake, 5, 8, 1, 7, plan.handle, fake, None) == -1
+    assert lib.tree_conv(fake, fake, None, fake, 5, 8, 5, 0, plan.handle, fake, None) == -1
+    assert lib.tree_conv(fake, fake, None, fake, 5, 8, 1, 0, plan.handle, None, None) == -1
+    scan = lib.tree_gdn_scan
+    args = [fake] * 7
+    assert scan(*args, 5, 2, 3, 128, 128, 1.0, 1, 0, plan.handle, fake, fake, 1 << 30, None) == -4
+    assert scan(*args, 5, 1, 1, 64, 64, 1.0, 1, 0, plan.handle, fake, fake, 1 << 30, None) == -4
+    assert scan(*args, 5, 1, 1, 128, 128, 1.0, 0, 0, plan.handle, fake, fake, 1 << 30, None) == -4
+    assert scan(*args, 4, 1, 1, 128, 128, 1.0, 1, 0, plan.handle, fake, fake, 1 << 30, None) == -3
+    assert scan(*args, 5, 1, 1, 128, 128, 1.0, 1, 9, plan.handle, fake, fake, 1 << 30, None) == -1
+    assert b"schedule" in lib.tree_last_error()
+
+
+def test_workspace_size_and_check():
+    lib = _lib.load()
+    parents, lens, _ = make_trie(2)
+    plan = _lib.TreePlan(parents, lens, 4)
+    need = lib.tree_scan_workspace_bytes(plan.handle, 16, 128, 128, 0)
+    assert need == 1 * 16 * 128 * 128 * 4  # one parent (the prompt)
+    assert lib.tree_scan_workspace_bytes(plan.handle, 16, 128, 128, 1) == 0
+    fake = ctypes.c_void_p(0x1000)
+    n = plan.n_tokens
+    rc = lib.tree_gdn_scan(*([fake] * 6), None, n, 16, 16, 128, 128, 1.0, 1, 0, plan.handle, fake,
+                           fake, need - 1, None)
+    assert rc == -5
+
+
+def test_library_shares_torchs_hip_runtime():
+    """The binding loads torch first so that the library's libamdhip64.so.7
+    dependency binds to torch's copy: one HIP runtime per process."""
+    _lib.load()
+    maps = open("/proc/self/maps").read()
+    hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(hip) == 1, hip
