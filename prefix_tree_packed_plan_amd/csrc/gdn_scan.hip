@@ -604,9 +604,7 @@ bool scan_supported(int d_k, int d_v, int dtype) {
 
 hipError_t launch_scan_level(const ScanArgs& a, int d_k, int d_v, int dtype, hipStream_t stream) {
   const bool f32 = dtype == TREE_DTYPE_F32;
-  const bool pair = (a.h_v / a.h_qk) % 2 == 0;  // two value heads share each q/k head
-  if (d_k == 128 && d_v == 128 && !f32)
-    return pair ? launch_one<128, 128, false, 2>(a, stream) : launch_one<128, 128, false, 1>(a, stream);
+  if (d_k == 128 && d_v == 128 && !f32) return launch_scan_d128(a, stream);
   if (d_k == 32 && d_v == 32)
     return f32 ? launch_one<32, 32, true, 1>(a, stream) : launch_one<32, 32, false, 1>(a, stream);
   return hipErrorInvalidValue;

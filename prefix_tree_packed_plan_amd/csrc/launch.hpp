@@ -48,6 +48,9 @@ struct ScanArgs {
 // hipErrorInvalidValue for a head size that is not compiled in.
 hipError_t launch_scan_level(const ScanArgs& a, int d_k, int d_v, int dtype, hipStream_t stream);
 
+// bf16, d_k = d_v = 128: the DMA-fed kernel (gdn_scan_d128.hip).
+hipError_t launch_scan_d128(const ScanArgs& a, hipStream_t stream);
+
 // Whether (d_k, d_v, dtype) has a compiled scan kernel.
 bool scan_supported(int d_k, int d_v, int dtype);
 
