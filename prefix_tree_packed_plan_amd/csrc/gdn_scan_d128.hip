@@ -77,6 +77,12 @@ __device__ __forceinline__ f32x4 mma16(const uint2 a, const uint2 b, const f32x4
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+// Sum over the 4 lanes of a quad (lanes 4k..4k+3), result in all four (DPP).
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+  return x;
+}
 
 // LDS tile of 64 x 128 bf16 (token x feature): 16 blocks of 4 rows, each
 // block 1 KB of data (one DMA instruction) plus 64 bytes of padding; row r4
@@ -315,19 +321,44 @@ __global__ __launch_bounds__(64 * NWV) void gdn_d128_kernel(ScanArgs args) {
       }
     }
 
-    // -- K S0 and Q S0; waves 0..3 also invert diagonal block cw of (I + A)
-    //    (fp32 forward substitution, lane = column), 4 rows per contraction
-    //    step so the dependent chain overlaps the MFMAs.
+    // -- inverse of diagonal block cw of (I + A), waves 0..3: fp32 forward
+    //    substitution T = (I + A_bb)^-1 with all 64 lanes: lane (j, p) =
+    //    (lane/4, lane%4) owns column j and the terms m = 4q + p of every row
+    //    sum; a row step is <= 4 FMAs and a quad sum, so the 15-step
+    //    dependent chain stays short, and the 36 entries a lane needs are
+    //    loaded before the chain starts.
+    if (cw < 4) {
+      const float* Ab = reinterpret_cast<const float*>(sm.a[blk(cw, cw)]);
+      const int jc = lane >> 2, ph = lane & 3;
+      float arow[16][4];
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr)
+#pragma unroll
+        for (int q = 0; 4 * q < rr; ++q) arow[rr][q] = Ab[bsw(rr, 4 * q + ph)];
+      float t[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t[q] = 4 * q + ph == jc ? 1.f : 0.f;
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr) {
+        // A_bb is strictly lower (zeros from the Gram tile), so the terms
+        // with 4q + ph >= rr read zeros and need no mask.
+        float part = 0.f;
+#pragma unroll
+        for (int q = 0; 4 * q < rr; ++q) part += arow[rr][q] * t[q];
+        const float sum = quad_sum(part);
+        const float val = rr > jc ? -sum : (rr == jc ? 1.f : 0.f);
+        if ((rr & 3) == ph) t[rr >> 2] = val;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sm.tb[cw][bsw(4 * q + ph, jc)] = split1(t[q]);
+    }
+
+    // -- K S0 and Q S0
     f32x4 R[4][NTW], O[4][NTW];
 #pragma unroll
     for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) R[mr][nt] = O[mr][nt] = zero4();
-    const bool inv = cw < 4;
-    const uint32_t* Ab = sm.a[blk(cw & 3, cw & 3)];
-    float tcol[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) tcol[m] = m == i16 ? 1.f : 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       uint4 sh[NTW], sl[NTW];
@@ -350,24 +381,6 @@ __global__ __launch_bounds__(64 * NWV) void gdn_d128_kernel(ScanArgs args) {
           O[mr][nt] = mma32(aq, sh[nt], O[mr][nt]);
         }
       }
-      if (inv) {
-#pragma unroll
-        for (int rr = 4 * kk + 1; rr <= 4 * kk + 4 && rr < 16; ++rr) {
-          float acc2 = 0.f;
-#pragma unroll
-          for (int q = 0; 4 * q < rr; ++q) {
-            const f32x4 row = *reinterpret_cast<const f32x4*>(&Ab[bsw(rr, 4 * q)]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (4 * q + e < rr) acc2 += row[e] * tcol[4 * q + e];
-          }
-          tcol[rr] = rr > i16 ? -acc2 : tcol[rr];
-        }
-      }
-    }
-    if (inv && h4 == 0) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.tb[cw][bsw(rr, i16)] = split1(tcol[rr]);
     }
 
     // -- R = diag(b) V - diag(b gamma) K S0; O = scale gamma Q S0
