@@ -43,7 +43,7 @@ def conv_bytes_per_token(s):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gdn_scan.hip", "tree_conv.hip"):
+    for f in ("gdn_scan.hip", "gdn_scan_d128.hip", "tree_conv.hip"):
         with open(os.path.join(ROOT, "prefix_tree_packed_plan_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -64,12 +64,14 @@ def load_traffic(kernel, workload):
     return entry.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s=20.0):
-    """The oracle as it stands, on one core, over a bounded sample: the first
-    root-to-leaf path, conv over all channels and the recurrence over as many
-    value heads as fit the time budget.  Scaled to the whole job (every path,
-    every head), since the oracle's cost is linear in path tokens x heads."""
-    import numpy as np
+def cpu_baseline(wl, budget_s=15.0):
+    """The oracle as it stands, on one core, over a bounded sample: whole
+    root-to-leaf paths (conv over all channels, the token-by-token recurrence
+    over all value heads) in leaf order until about `budget_s` seconds of
+    work.  Scaled to the whole job (every path), since the oracle's cost is
+    linear in path tokens."""
+    import numpy as np  # noqa: F401
+    import torch
     from threadpoolctl import threadpool_limits
 
     from oracle import conv as oconv
@@ -78,34 +80,31 @@ def cpu_baseline(wl, budget_s=20.0):
 
     s = wl.spec
     t = wl.tensors
-    path = otrie.leaf_paths(wl.parents)[0]
-    idx = otrie.path_token_index(path, wl.seg_lens)
-    import torch
-    it = torch.as_tensor(idx, device=t["x"].device)
-    host = {k: v.index_select(0, it).double().cpu().numpy() for k, v in t.items() if k != "w"}
     w = t["w"].double().cpu().numpy()
     total_path = otrie.path_token_count(wl.parents, wl.seg_lens)
+    done_tok, spent, n_paths = 0, 0.0, 0
     with threadpool_limits(1):
-        t0 = time.perf_counter()
-        oconv.conv_on_path(host["x"], w)
-        t_conv = time.perf_counter() - t0
-        heads_done, t_scan = 0, 0.0
-        L = len(idx)
-        while heads_done < s.h_v and t_scan < budget_s:
+        for path in otrie.leaf_paths(wl.parents):
+            idx = otrie.path_token_index(path, wl.seg_lens)
+            it = torch.as_tensor(idx, device=t["x"].device)
+            host = {k: v.index_select(0, it).double().cpu().numpy() for k, v in t.items() if k != "w"}
             t0 = time.perf_counter()
-            ogdn.gdn_on_path(host["q"], host["k"], host["v"], host["g"], host["beta"],
-                             heads=[heads_done])
-            t_scan += time.perf_counter() - t0
-            heads_done += 1
-    full_s = (t_conv + t_scan * s.h_v / heads_done) * total_path / L
+            oconv.conv_on_path(host["x"], w)
+            ogdn.gdn_on_path(host["q"], host["k"], host["v"], host["g"], host["beta"])
+            spent += time.perf_counter() - t0
+            done_tok += len(idx)
+            n_paths += 1
+            if spent >= budget_s:
+                break
+    full_s = spent * total_path / done_tok
     return {
         "value": wl.n_tokens / full_s,
         "unit": "unique tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"first root-to-leaf path ({L} tokens of {total_path} path tokens): conv over all "
-                   f"{s.channels} channels and the token-by-token recurrence for {heads_done} of {s.h_v} "
-                   f"value heads, {t_conv + t_scan:.1f} s on 1 core; scaled linearly to every path and head"),
+        "sample": (f"{n_paths} whole root-to-leaf paths ({done_tok} of {total_path} path tokens): conv over all "
+                   f"{s.channels} channels and the token-by-token recurrence over all {s.h_v} value heads, "
+                   f"{spent:.1f} s on 1 core (fp64 NumPy); scaled linearly to every path"),
     }
 
 
@@ -116,6 +115,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="before timing, run one plain 1 GiB device copy (a counter reference for profiles)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the tree forward here is a single-GPU path "
@@ -138,6 +139,10 @@ def main():
     ws_bytes = int(lib.tree_scan_workspace_bytes(plan.handle, s.h_v, s.d_k, s.d_v, 0))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     plan.on_device(dev)
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        del src
     torch.cuda.synchronize()
 
     def step(ev=None):
