@@ -1,7 +1,7 @@
 // Chunked tree Gated DeltaNet forward for bf16, d_k = d_v = 128, on gfx950.
 //
 // Method ("Tree Training", arXiv 2511.00413, section 3.2 Eq. 10 and the
-// chunked form of appendix A.2), per 64-token chunk of one segment and one
+// chunked form of appendix A.2), per 32-token chunk of one segment and one
 // value head, with G the in-chunk prefix of g, gamma = exp(G), b = beta:
 //     A_ij = b_i exp(G_i - G_j) k_i.k_j  (j < i),   T = (I + A)^-1,
 //     R = diag(b) V - diag(b gamma) K S0,   U = T R,
@@ -12,37 +12,35 @@
 //
 // Work-group = one (segment, value head), 8 waves; wave w owns value columns
 // [16w, 16w + 16) and keeps that 128 x 16 slice of the fp32 state in MFMA
-// accumulator registers for the whole segment.  Per chunk:
+// accumulator registers for the whole segment.  Registers are held to 128
+// per lane and LDS to 72 KB so that two work-groups share a compute unit;
+// their phases drift apart, so one's MFMA work fills the other's latency.
+// Per chunk:
 //
 //   prep (no state needed)   every wave: its own copy of the gate prefix
-//                            (DPP scan).  Waves 0 and 1: the three K K^T
-//                            tiles of one 32-token half, the two 16 x 16
-//                            diagonal inverses (fp32 forward substitution)
-//                            and the off-diagonal block -T_bb A_ba T_aa, i.e.
-//                            the 32 x 32 inverse of that half.  Waves 2..7:
-//                            the K K^T tiles coupling the halves and the
-//                            Q K^T tiles.  All land in LDS as ready-made MFMA
+//                            (DPP scan).  Waves 0 and 1: one 16 x 16 diagonal
+//                            block of K K^T each and its inverse (I + A_bb)^-1
+//                            (fp32 forward substitution).  Wave 2: the
+//                            off-diagonal block A_10.  Waves 3, 6, 7: the three
+//                            Q K^T blocks.  All land in LDS as ready-made MFMA
 //                            operands, split hi + lo where they feed the state.
-//   state, part 1            R = diag(b)(V - gamma K S0) and O^T = S0^T Q^T
-//                            (overlaps the prep of waves 0 and 1).
+//   state, part 1            R = diag(b)(V - gamma K S0) and O^T = S0^T Q^T.
 //   ---- barrier ----
-//   state, part 2            two-level solve: U_top = T_top R_top,
-//                            R_bot -= A_bt U_top, U_bot = T_bot R_bot; then
-//                            O^T += U^T P^T and S = gamma_L S + K^T W.
+//   state, part 2            U_0 = T_00 R_0, R_1 -= A_10 U_0, U_1 = T_11 R_1;
+//                            O^T += U^T P^T;  S = gamma_L S + K^T W.
 //
-// Every product runs on v_mfma_f32_16x16x32_bf16 except the two 16 x 16 x 16
-// steps of the off-diagonal inverse block.  Products that feed the state carry
-// their fp32 operand as hi + lo bf16 (relative 2^-17; lo x lo dropped); the
-// output path uses hi only.  The output is produced transposed, so a lane
-// holds 4 consecutive value columns of one token and stores 8 bytes.
+// Products that feed the state carry their fp32 operand as hi + lo bf16
+// (relative 2^-17; lo x lo dropped); the output path uses hi only.  The
+// output is produced transposed, so a lane holds 4 consecutive value columns
+// of one token.
 //
 // Data movement: q, k, v, g and beta of chunk n + 1 are DMA'd from HBM into
-// LDS (global_load_lds, 16 bytes per lane, no staging registers) at the start
-// of chunk n, into the other half of double buffers, so the loads have a
-// whole chunk to land.  The output of chunk n is staged in LDS and leaves as
-// whole 256-byte token rows during chunk n + 1.  Both go through buffer descriptors, so
-// per-lane offsets are loop constants and masked output rows are dropped by
-// the descriptor's range check.
+// LDS (buffer loads straight to LDS, 16 bytes per lane, no staging registers)
+// at the start of chunk n, into the other half of double buffers.  The output
+// of chunk n is staged in LDS and leaves as whole 256-byte token rows during
+// chunk n + 1.  Loads and stores go through buffer descriptors, so per-lane
+// offsets are loop constants and masked output rows are dropped by the
+// descriptor's range check.
 //
 // Tile layout in LDS (see toff): rows in 4-row blocks of 1 KB (one DMA
 // instruction each) at a 1088-byte stride, block b shifted by a further
@@ -68,10 +66,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int CH = 64;   // chunk length (tokens)
-constexpr int D = 128;   // d_k = d_v
-constexpr int NW = 8;    // waves per work-group
-constexpr int TSZ = 17408;      // LDS bytes of one 64 x 128 bf16 tile (see toff)
+constexpr int CH = 32;          // chunk length (tokens)
+constexpr int D = 128;          // d_k = d_v
+constexpr int NW = 8;           // waves per work-group
+constexpr int TSZ = 8704;       // LDS bytes of one 32 x 128 bf16 tile (see toff)
+constexpr int ROW16 = 4352;     // bytes between rows 16 apart
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint32_t pk2(float a, float b) {
@@ -101,14 +100,15 @@ __device__ __forceinline__ f32x4 mma16(const uint2 a, const uint2 b, const f32x4
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
                                                    0, 0, 0);
 }
-// hi x hi + hi x lo + lo x hi.
-__device__ __forceinline__ f32x4 mma32x3(const uint4 ah, const uint4 al, const uint4 bh, const uint4 bl, f32x4 c) {
-  c = mma32(ah, bh, c);
-  c = mma32(ah, bl, c);
-  return mma32(al, bh, c);
+// hi x hi + hi x lo + lo x hi (K = 16).
+__device__ __forceinline__ f32x4 mma16x3(const uint2 ah, const uint2 al, const uint2 bh, const uint2 bl, f32x4 c) {
+  c = mma16(ah, bh, c);
+  c = mma16(ah, bl, c);
+  return mma16(al, bh, c);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+// Lane i gets lane i - n of its row of 16 (0 for the first n lanes of a row).
 __device__ __forceinline__ float dpp_shr(float x, int n) {
   switch (n) {
     case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
@@ -124,14 +124,12 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
-// ---- 64 x 128 bf16 tiles in LDS ------------------------------------------------
+// ---- 32 x 128 bf16 tiles in LDS ------------------------------------------------
 // Byte offset of the 4-row block b, and of element (row, col).
 __device__ __forceinline__ int blk_off(int b) { return b * 1088 + 16 * ((0x3120 >> (4 * (b & 3))) & 3); }
 __device__ __forceinline__ int toff(int row, int col) {
   return blk_off(row >> 2) + (row & 3) * 256 + 16 * ((col >> 3) ^ (4 * (row & 3))) + 2 * (col & 7);
 }
-// Rows 16 apart are 4352 bytes apart (the block shifts repeat every 4 blocks).
-constexpr int ROW16 = 4352;
 // A operand of a 16x16x32 MFMA (or the B operand, the roles are symmetric)
 // at byte offset `o` = toff(row, col0 + 4h): row `row`, columns
 // col0 + kmap(h, 0..7), kmap(h, j) = j<4 ? 4h+j : 16+4h+(j-4); the two 8-byte
@@ -151,21 +149,16 @@ __device__ __forceinline__ uint2 ld_tr(const char* t, int o) {
 }
 __device__ __forceinline__ f32x4 bf4(const uint2 x) { return f32x4{lo_f(x.x), hi_f(x.x), lo_f(x.y), hi_f(x.y)}; }
 
-// 16x16 fp32 blocks, row-major, 4-float groups permuted by row / 4.
-__device__ __forceinline__ int aoff(int r, int c) { return r * 16 + 4 * ((c >> 2) ^ ((r >> 2) & 3)) + (c & 3); }
-
 struct Smem {
   alignas(16) char kb[2][TSZ];       // K tiles
   alignas(16) char qb[2][TSZ];       // Q tiles
   alignas(16) char vb[2][TSZ];       // V tiles
-  // A operands, per lane, hi and lo: 0..3 = row block b of the two 32 x 32
-  // inverses (b = 0, 1: T_top; b = 2, 3: T_bot); 4, 5 = -A rows 32..47 and
-  // 48..63, columns 0..31.
-  alignas(16) uint4 ttab[6][2][64];
-  // B operands of O^T += U^T P^T: (j-half p, row block b) = (0,0) (0,1) (0,2) (1,2) (0,3) (1,3).
-  alignas(16) uint4 ptab[6][64];
-  alignas(16) float abb[2][2][256];  // waves 0, 1: gated diagonal K K^T blocks
-  alignas(16) float tbb[2][2][256];  // waves 0, 1: (I + A_bb)^-1
+  // 16x16x16 A operands per lane, [hi, lo]: 0 = T_00, 1 = T_11, 2 = -A_10.
+  alignas(16) uint2 ttab[3][2][64];
+  // 16x16x32 B operands of O^T += U^T P^T for token blocks 0 and 1.
+  alignas(16) uint4 ptab[2][64];
+  // Waves 0, 1: their gated diagonal block, A[r][4q + p] at [r][p][q].
+  alignas(16) float abb[2][256];
   alignas(16) float gt[NW][4][CH];   // per wave: G log2(e), exp(G), beta, exp(G_L - G)
   alignas(16) float graw[2][CH];
   alignas(16) float braw[2][CH];
@@ -178,31 +171,16 @@ struct Smem {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes), 0x00020000);
 }
-// DMA of the 4-row blocks first, first + step, ... of a 64 x 128 bf16 tile:
-// lane l loads the 16-byte chunk (l % 16) ^ 4(l / 16) of row 4b + l / 16,
-// which the layout puts at LDS byte 16 l of the block.  `voff` is that
-// lane's byte offset for b = 0; `rstride` the bytes between rows.
-__device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t r, int voff, int rstride, char* tile, int first,
-                                         int step) {
-  for (int b = first; b < 16; b += step)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + blk_off(b)), 16, voff, 4 * b * rstride, 0, 0);
-}
-// Same for a partial chunk of Ln rows: rows past the end repeat row Ln - 1.
-__device__ __forceinline__ void dma_tile_tail(__amdgpu_buffer_rsrc_t r, int coff, int rstride, int Ln, char* tile,
-                                              int first, int step, int lane) {
-  for (int b = first; b < 16; b += step)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + blk_off(b)), 16,
-                                             min(4 * b + (lane >> 4), Ln - 1) * rstride + coff, 0, 0, 0);
-}
 
-// Raw 16 x 16 Gram tile D[x][y] = X[16xb + x] . Y[16yb + y] over 128
-// features: lane (y = i, h) holds x = 4h + 0..3.  ao[kk] = toff(i, 32kk + 4h).
-__device__ __forceinline__ f32x4 gram(const char* X, int xb, const char* Y, int yb, const int* ao) {
+// Raw 16 x 16 Gram tile D[x][y] = X[x] . Y[y] over 128 features (X, Y point
+// at row blocks of tiles): lane (y = i, h) holds x = 4h + 0..3.
+// ao[kk] = toff(i, 32kk + 4h).
+__device__ __forceinline__ f32x4 gram(const char* X, const char* Y, const int* ao) {
   uint4 a[4], b[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    a[kk] = ld_a8(X + ROW16 * xb, ao[kk]);
-    b[kk] = ld_a8(Y + ROW16 * yb, ao[kk]);
+    a[kk] = ld_a8(X, ao[kk]);
+    b[kk] = ld_a8(Y, ao[kk]);
   }
   f32x4 acc = zero4();
 #pragma unroll
@@ -210,20 +188,7 @@ __device__ __forceinline__ f32x4 gram(const char* X, int xb, const char* Y, int 
   return acc;
 }
 
-// Gram tiles of waves 2..7: kind (0: -A block, 1: P^T block), key block jb,
-// query/row block ib.  Waves 4 and 5 share SIMDs with waves 0 and 1 and get
-// one tile each, the others three.
-__device__ __forceinline__ int tile_code(int idx) {
-  // (kind << 4) | (jb << 2) | ib
-  constexpr int codes[14] = {(0 << 4) | (0 << 2) | 2, (0 << 4) | (1 << 2) | 2, (0 << 4) | (0 << 2) | 3,
-                             (0 << 4) | (1 << 2) | 3, (1 << 4) | (0 << 2) | 0, (1 << 4) | (0 << 2) | 1,
-                             (1 << 4) | (1 << 2) | 1, (1 << 4) | (0 << 2) | 2, (1 << 4) | (1 << 2) | 2,
-                             (1 << 4) | (2 << 2) | 2, (1 << 4) | (0 << 2) | 3, (1 << 4) | (1 << 2) | 3,
-                             (1 << 4) | (2 << 2) | 3, (1 << 4) | (3 << 2) | 3};
-  return codes[idx];
-}
-
-__global__ __launch_bounds__(64 * NW) void gdn_d128_kernel(ScanArgs args) {
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4))) void gdn_d128_kernel(ScanArgs args) {
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
@@ -260,9 +225,9 @@ __global__ __launch_bounds__(64 * NW) void gdn_d128_kernel(ScanArgs args) {
   const int col_w = 16 * cw;
   float* gtw = &sm.gt[cw][0][0];  // this wave's gate tables
 
-  // Loop-constant byte offsets: operand reads of rows i16 (+16 per row
-  // block) at columns 32kk + 4h4; transposing reads of K at columns 32m (+16
-  // is +32 bytes) and of V at this wave's columns; DMA and output lanes.
+  // Loop-constant byte offsets of the hot reads: operand reads of rows i16
+  // (+16 per row block) at columns 32kk + 4h4; transposing reads of K at
+  // columns 32m (+16 is +32 bytes) and of V at this wave's columns.
   int ao[4], ko[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -271,19 +236,6 @@ __global__ __launch_bounds__(64 * NW) void gdn_d128_kernel(ScanArgs args) {
   }
   const int vo = toff(4 * h4 + (i16 >> 2), col_w + 4 * (i16 & 3));
   const int rs_qk = args.h_qk * D * 2, rs_v = args.h_v * D * 2;  // bytes between token rows
-  const int cofs = 16 * ((lane & 15) ^ (4 * (lane >> 4)));        // this lane's 16-byte chunk of a row
-  const int voff_qk = (lane >> 4) * rs_qk + cofs, voff_v = (lane >> 4) * rs_v + cofs;
-  // Output staging: this lane writes token 16b + i16, value columns
-  // col_w + 4h4..+3 (8 bytes); it later stores 16-byte chunk lane % 16 of
-  // token rows 8cw + lane / 16 (+4).
-  const int sto_w = i16 * 256 + 16 * ((2 * cw + (h4 >> 1)) ^ i16) + 8 * (h4 & 1);
-  int sto_r[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int row = 8 * cw + (lane >> 4) + 4 * k;
-    sto_r[k] = row * 256 + 16 * ((lane & 15) ^ (row & 15));
-  }
-  const int ooff = (8 * cw + (lane >> 4)) * rs_v + 16 * (lane & 15);
 
   // ---- initial state: S[mt] rows 16mt + 4h4 + 0..3, column col_w + i16 --------
   const size_t head_elems = static_cast<size_t>(D) * D;
@@ -304,40 +256,43 @@ __global__ __launch_bounds__(64 * NW) void gdn_d128_kernel(ScanArgs args) {
     }
   }
 
-  // Chunk at token tc into buffer buf: 48 tile blocks and two gate rows.
+  // Chunk at token tc into buffer buf: wave cw loads block cw (rows
+  // 4cw..4cw+3) of the K, Q and V tiles; waves 4 and 5 the gate rows.  In a
+  // partial chunk, rows past the end repeat row Ln - 1.
   auto fetch = [&](int tc, int buf) {
+    // Offsets of once-per-chunk accesses are recomputed from an opaque copy
+    // of the lane number rather than held in registers across the loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int cofs = 16 * ((ln & 15) ^ (4 * (ln >> 4)));  // this lane's 16-byte chunk of a row
     const int Ln = min(CH, seg_end - tc);
     const auto rk = rsrc(kg + (static_cast<size_t>(tc) * args.h_qk + hq) * D, CH * rs_qk);
     const auto rq = rsrc(qg + (static_cast<size_t>(tc) * args.h_qk + hq) * D, CH * rs_qk);
     const auto rv = rsrc(vg + (static_cast<size_t>(tc) * args.h_v + h) * D, CH * rs_v);
-    if (Ln == CH) {
-      dma_tile(rk, voff_qk, rs_qk, sm.kb[buf], cw, NW);
-      dma_tile(rq, voff_qk, rs_qk, sm.qb[buf], cw, NW);
-      dma_tile(rv, voff_v, rs_v, sm.vb[buf], cw, NW);
-    } else {
-      dma_tile_tail(rk, cofs, rs_qk, Ln, sm.kb[buf], cw, NW, lane);
-      dma_tile_tail(rq, cofs, rs_qk, Ln, sm.qb[buf], cw, NW, lane);
-      dma_tile_tail(rv, cofs, rs_v, Ln, sm.vb[buf], cw, NW, lane);
-    }
-    if (cw >= NW - 2) {
-      const float* src = (cw == NW - 1 ? args.beta : args.g) + static_cast<size_t>(tc) * args.h_v + h;
+    const int row = min(4 * cw + (ln >> 4), Ln - 1);  // block cw of each tile
+    const int ok = row * rs_qk + cofs, ov = row * rs_v + cofs;
+    const int lo = blk_off(cw);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sm.kb[buf] + lo), 16, ok, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sm.qb[buf] + lo), 16, ok, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sm.vb[buf] + lo), 16, ov, 0, 0, 0);
+    if ((cw == 4 || cw == 5) && lane < CH) {  // lane l writes LDS word l of the row
+      const float* src = (cw == 5 ? args.beta : args.g) + static_cast<size_t>(tc) * args.h_v + h;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(src, CH * args.h_v * 4),
-                                               (lds_void*)(cw == NW - 1 ? sm.braw[buf] : sm.graw[buf]), 4,
+                                               (lds_void*)(cw == 5 ? sm.braw[buf] : sm.graw[buf]), 4,
                                                min(lane, Ln - 1) * args.h_v * 4, 0, 0, 0);
     }
   };
 
-  // Output of the previous chunk (transposed tiles packed to bf16): token
-  // 16b + i16, value columns col_w + 4h4 + 0..3.
   // Whole token rows of the staged output; the descriptor ends after row
   // Ln - 1, so rows past it are not written.
+  // This lane stores 16-byte chunk lane % 16 of token row 4cw + lane / 16.
   auto store_out = [&](int tc, int Ln) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int orow = 4 * cw + (ln >> 4);
     const auto ro = rsrc(og + (static_cast<size_t>(tc) * args.h_v + h) * D, (Ln - 1) * rs_v + D * 2);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(sm.ost + sto_r[k]);
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, ooff + 4 * k * rs_v, 0, 0);
-    }
+    const u32x4 v = *reinterpret_cast<const u32x4*>(sm.ost + orow * 256 + 16 * ((ln & 15) ^ (orow & 15)));
+    __builtin_amdgcn_raw_buffer_store_b128(v, ro, orow * rs_v + 16 * (ln & 15), 0, 0);
   };
 
   fetch(seg_beg, 0);
@@ -354,233 +309,180 @@ __global__ __launch_bounds__(64 * NW) void gdn_d128_kernel(ScanArgs args) {
     __syncthreads();                                   // (A) ... and every other wave's
     if (t0 + CH < seg_end) fetch(t0 + CH, s ^ 1);
 
-    // -- gates, per wave: inclusive prefix of g within rows of 16 lanes (DPP),
-    //    then across rows
+    // -- gates, per wave: inclusive prefix of g over rows of 16 lanes (DPP),
+    //    then row 1 adds row 0's total
     {
-      float x = lane < Lc ? sm.graw[s][lane] : 0.f;
+      float x = lane < Lc ? sm.graw[s][lane & (CH - 1)] : 0.f;
       x += dpp_shr(x, 1);
       x += dpp_shr(x, 2);
       x += dpp_shr(x, 4);
       x += dpp_shr(x, 8);
-      const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
-      const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
-      const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
-      const int row = lane >> 4;
-      x += (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
+      x += lane >= 16 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15)) : 0.f;
       const float g2 = x * kLog2e;
-      const float g2L = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), 63));
-      gtw[lane] = g2;
-      gtw[CH + lane] = ex2(g2);
-      gtw[2 * CH + lane] = lane < Lc ? sm.braw[s][lane] : 0.f;
-      gtw[3 * CH + lane] = ex2(g2L - g2);
+      const float g2L = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), CH - 1));
+      if (lane < CH) {
+        gtw[lane] = g2;
+        gtw[CH + lane] = ex2(g2);
+        gtw[2 * CH + lane] = lane < Lc ? sm.braw[s][lane] : 0.f;
+        gtw[3 * CH + lane] = ex2(g2L - g2);
+      }
     }
     asm volatile("" ::: "memory");
 
     // -- prep
     if (cw < 2) {
-      // 32 x 32 inverse of rows/columns 32cw .. 32cw + 31.
-      const int ba = 2 * cw, bb = 2 * cw + 1;
-      const f32x4 daa = gram(Ks, ba, Ks, ba, ao);  // lane i, rows j
-      const f32x4 dbb = gram(Ks, bb, Ks, bb, ao);
-      const f32x4 dba = gram(Ks, bb, Ks, ba, ao);  // lane j (block a), rows i (block b)
+      // Diagonal block cw: A[i][j] = b_i exp(G_i - G_j) k_i.k_j (j < i) and
+      // T = (I + A)^-1 by fp32 forward substitution, lane (j, p) =
+      // (lane/4, lane%4) owning column j and the terms m = 4q + p of every
+      // row sum, so a step is <= 4 FMAs and a quad sum.
+      const f32x4 d = gram(Ks + ROW16 * cw, Ks + ROW16 * cw, ao);  // lane i, rows j
       {
+        const float gi = gtw[16 * cw + i16];
+        const float bi = gtw[2 * CH + 16 * cw + i16];
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&gtw[16 * cw + 4 * h4]);
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          const int ib = ba + blk;
-          const f32x4 d = blk ? dbb : daa;
-          const float gi = gtw[16 * ib + i16];
-          const float bi = gtw[2 * CH + 16 * ib + i16];
-          const f32x4 gj = *reinterpret_cast<const f32x4*>(&gtw[16 * ib + 4 * h4]);
-          f32x4 v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = 4 * h4 + r < i16 ? bi * d[r] * ex2(gi - gj[r]) : 0.f;
-          *reinterpret_cast<f32x4*>(&sm.abb[cw][blk][aoff(i16, 4 * h4)]) = v;
-        }
-      }
-      f32x4 aba;  // A_ba[4h4 + r][i16] (rows in block b, column in block a)
-      {
-        const float gj = gtw[16 * ba + i16];
-        const f32x4 gi = *reinterpret_cast<const f32x4*>(&gtw[16 * bb + 4 * h4]);
-        const f32x4 bi = *reinterpret_cast<const f32x4*>(&gtw[2 * CH + 16 * bb + 4 * h4]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) aba[r] = bi[r] * dba[r] * ex2(gi[r] - gj);
+        for (int r = 0; r < 4; ++r)
+          sm.abb[cw][i16 * 16 + r * 4 + h4] = 4 * h4 + r < i16 ? bi * d[r] * ex2(gi - gj[r]) : 0.f;
       }
       asm volatile("" ::: "memory");
-      // (I + A_bb)^-1 of both diagonal blocks, fp32 forward substitution with
-      // lane (j, p) = (lane/4, lane%4) owning column j and the terms m = 4q + p
-      // of every row sum (a step is <= 4 FMAs and a quad sum per block).
-      {
-        const int jc = lane >> 2, ph = lane & 3;
-        float arow[2][16][4];
+      const int jc = lane >> 2, ph = lane & 3;
+      // Row rr needs the terms q < ceil(rr / 4) only.
+      float arow[16][4];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int rr = 1; rr < 16; ++rr)
-#pragma unroll
-            for (int q = 0; 4 * q < rr; ++q) arow[blk][rr][q] = sm.abb[cw][blk][aoff(rr, 4 * q + ph)];
-        float t[2][4];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) t[blk][q] = 4 * q + ph == jc ? 1.f : 0.f;
-#pragma unroll
-        for (int rr = 1; rr < 16; ++rr) {
-#pragma unroll
-          for (int blk = 0; blk < 2; ++blk) {
-            // A_bb is strictly lower (zeros from the gated tile), so terms with
-            // 4q + ph >= rr read zeros and need no mask.
-            float part = 0.f;
-#pragma unroll
-            for (int q = 0; 4 * q < rr; ++q) part += arow[blk][rr][q] * t[blk][q];
-            const float sum = quad_sum(part);
-            const float val = rr > jc ? -sum : (rr == jc ? 1.f : 0.f);
-            if ((rr & 3) == ph) t[blk][rr >> 2] = val;
-          }
-        }
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) sm.tbb[cw][blk][aoff(4 * q + ph, jc)] = t[blk][q];
-      }
-      asm volatile("" ::: "memory");
-      // Tiles of the 32 x 32 inverse [[T_aa, 0], [X, T_bb]], X = -T_bb A_ba T_aa.
-      {
-        const f32x4 ta = *reinterpret_cast<const f32x4*>(&sm.tbb[cw][0][aoff(i16, 4 * h4)]);  // T_aa[i16][4h4..]
-        const f32x4 tb = *reinterpret_cast<const f32x4*>(&sm.tbb[cw][1][aoff(i16, 4 * h4)]);  // T_bb[i16][4h4..]
-        f32x4 tat;                                                                             // T_aa[4h4..][i16]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tat[r] = sm.tbb[cw][0][aoff(4 * h4 + r, i16)];
-        uint2 tah, tal, tbh, tbl, tath, tatl, abh, abl;
-        split4(ta, tah, tal);
-        split4(tb, tbh, tbl);
-        split4(tat, tath, tatl);
-        split4(aba, abh, abl);
-        // Z = A_ba^T T_bb^T, X^T = -T_aa^T Z
-        f32x4 z = mma16(abh, tbh, zero4());
-        z = mma16(abh, tbl, z);
-        z = mma16(abl, tbh, z);
-        uint2 zh, zl;
-        split4(z, zh, zl);
-        f32x4 xt = mma16(tath, zh, zero4());
-        xt = mma16(tath, zl, xt);
-        xt = mma16(tatl, zh, xt);
-        uint2 xh, xl;
-        split4(-xt, xh, xl);
-        sm.ttab[ba][0][lane] = make_uint4(tah.x, tah.y, 0u, 0u);
-        sm.ttab[ba][1][lane] = make_uint4(tal.x, tal.y, 0u, 0u);
-        sm.ttab[bb][0][lane] = make_uint4(xh.x, xh.y, tbh.x, tbh.y);
-        sm.ttab[bb][1][lane] = make_uint4(xl.x, xl.y, tbl.x, tbl.y);
-      }
-    } else {
-      const int first = cw == 4 ? 12 : cw == 5 ? 13 : (cw < 4 ? cw - 2 : cw - 4);  // 0,1,(12),(13),2,3
-#pragma unroll
-      for (int it = 0; it < 3; ++it) {
-        if (it > 0 && (cw == 4 || cw == 5)) break;
-        const int idx = first + 4 * it;  // waves 2,3,6,7: idx, idx + 4, idx + 8
-        const int code = tile_code(idx);
-        const int kind = code >> 4, jb = (code >> 2) & 3, ib = code & 3;
-        const f32x4 d = gram(Ks, jb, kind ? Qs : Ks, ib, ao);  // lane i (block ib), rows j (block jb)
-        const float gi = gtw[16 * ib + i16];
-        const f32x4 gj = *reinterpret_cast<const f32x4*>(&gtw[16 * jb + 4 * h4]);
-        if (kind == 0) {
-          const float bi = gtw[2 * CH + 16 * ib + i16];
-          f32x4 v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = -bi * d[r] * ex2(gi - gj[r]);
-          uint2 vh, vl;
-          split4(v, vh, vl);
-          reinterpret_cast<uint2*>(&sm.ttab[4 + ib - 2][0][lane])[jb & 1] = vh;
-          reinterpret_cast<uint2*>(&sm.ttab[4 + ib - 2][1][lane])[jb & 1] = vl;
+      for (int rr = 1; rr < 16; ++rr) {
+        const float* pa = &sm.abb[cw][rr * 16 + ph * 4];
+        if (rr <= 4) {
+          arow[rr][0] = pa[0];
+        } else if (rr <= 8) {
+          const float2 v = *reinterpret_cast<const float2*>(pa);
+          arow[rr][0] = v.x, arow[rr][1] = v.y;
         } else {
-          f32x4 v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = 16 * jb + 4 * h4 + r <= 16 * ib + i16 ? args.scale * d[r] * ex2(gi - gj[r]) : 0.f;
-          const int pp = ib < 2 ? ib : 2 * ib - 2 + (jb >> 1);
-          reinterpret_cast<uint2*>(&sm.ptab[pp][lane])[jb & 1] = make_uint2(pk2(v[0], v[1]), pk2(v[2], v[3]));
-          if (jb == ib && (jb & 1) == 0)  // the other half of this operand is above the diagonal
-            reinterpret_cast<uint2*>(&sm.ptab[pp][lane])[1] = make_uint2(0u, 0u);
+          const float4 v = *reinterpret_cast<const float4*>(pa);
+          arow[rr][0] = v.x, arow[rr][1] = v.y, arow[rr][2] = v.z, arow[rr][3] = v.w;
         }
       }
+      float t[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) t[q] = 4 * q + ph == jc ? 1.f : 0.f;
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr) {
+        // A is strictly lower (zeros from the gated tile), so terms with
+        // 4q + ph >= rr read zeros and need no mask.
+        float part = 0.f;
+#pragma unroll
+        for (int q = 0; 4 * q < rr; ++q) part += arow[rr][q] * t[q];
+        const float sum = quad_sum(part);
+        const float val = rr > jc ? -sum : (rr == jc ? 1.f : 0.f);
+        if ((rr & 3) == ph) t[rr >> 2] = val;
+      }
+      // T[4q + ph][jc] -> operand lane (row 4q + ph, group jc / 4), element jc % 4.
+      uint16_t* th = reinterpret_cast<uint16_t*>(&sm.ttab[cw][0][0]);
+      uint16_t* tl = reinterpret_cast<uint16_t*>(&sm.ttab[cw][1][0]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = (4 * q + ph + 16 * (jc >> 2)) * 4 + (jc & 3);
+        const uint32_t w = pk2(t[q], 0.f);
+        th[e] = static_cast<uint16_t>(w);
+        tl[e] = static_cast<uint16_t>(pk2(t[q] - lo_f(w), 0.f));
+      }
+    } else if (cw == 2) {
+      // -A_10 as the A operand of R_1 -= A_10 U_0: lane i (token 16 + i),
+      // rows j (tokens 0..15).
+      const f32x4 d = gram(Ks, Ks + ROW16, ao);
+      const float gi = gtw[16 + i16];
+      const float bi = gtw[2 * CH + 16 + i16];
+      const f32x4 gj = *reinterpret_cast<const f32x4*>(&gtw[4 * h4]);
+      f32x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = -bi * d[r] * ex2(gi - gj[r]);
+      uint2 vh, vl;
+      split4(v, vh, vl);
+      sm.ttab[2][0][lane] = vh;
+      sm.ttab[2][1][lane] = vl;
+    } else if (cw == 3 || cw >= 6) {
+      // P^T block (jb, ib) = (0, 0), (0, 1), (1, 1): lane i (query), rows j (key).
+      const int jb = cw == 7 ? 1 : 0, ib = cw == 3 ? 0 : 1;
+      const f32x4 d = gram(Ks + ROW16 * jb, Qs + ROW16 * ib, ao);
+      const float gi = gtw[16 * ib + i16];
+      const f32x4 gj = *reinterpret_cast<const f32x4*>(&gtw[16 * jb + 4 * h4]);
+      f32x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        v[r] = 16 * jb + 4 * h4 + r <= 16 * ib + i16 ? args.scale * d[r] * ex2(gi - gj[r]) : 0.f;
+      reinterpret_cast<uint2*>(&sm.ptab[ib][lane])[jb] = make_uint2(pk2(v[0], v[1]), pk2(v[2], v[3]));
+      if (ib == 0)  // the other half of this operand is above the diagonal
+        reinterpret_cast<uint2*>(&sm.ptab[0][lane])[1] = make_uint2(0u, 0u);
     }
 
     // -- state, part 1: R = diag(b)(V - gamma K S0), O^T = scale gamma (S0^T Q^T)
-    f32x4 R[4], OT[4];
-    {
-      uint4 sh[4], sl[4];
+    f32x4 R[2], OT[2];
+    R[0] = R[1] = OT[0] = OT[1] = zero4();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) split8(S[2 * kk], S[2 * kk + 1], sh[kk], sl[kk]);
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 sh, sl;
+      split8(S[2 * kk], S[2 * kk + 1], sh, sl);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) R[b] = OT[b] = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint4 ak = ld_a8(Ks + ROW16 * b, ao[kk]);
-          const uint4 aq = ld_a8(Qs + ROW16 * b, ao[kk]);
-          R[b] = mma32(ak, sh[kk], R[b]);
-          R[b] = mma32(ak, sl[kk], R[b]);
-          OT[b] = mma32(sh[kk], aq, OT[b]);
-        }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(&gtw[CH + 16 * b + 4 * h4]);
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(&gtw[2 * CH + 16 * b + 4 * h4]);
-        const f32x4 vv = bf4(ld_tr(Vs + ROW16 * b, vo));
-        R[b] = bv * (vv - gv * R[b]);
-        OT[b] *= args.scale * gtw[CH + 16 * b + i16];
+      for (int b = 0; b < 2; ++b) {
+        const uint4 ak = ld_a8(Ks + ROW16 * b, ao[kk]);
+        const uint4 aq = ld_a8(Qs + ROW16 * b, ao[kk]);
+        R[b] = mma32(ak, sh, R[b]);
+        R[b] = mma32(ak, sl, R[b]);
+        OT[b] = mma32(sh, aq, OT[b]);
       }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(&gtw[CH + 16 * b + 4 * h4]);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(&gtw[2 * CH + 16 * b + 4 * h4]);
+      const f32x4 vv = bf4(ld_tr(Vs + ROW16 * b, vo));
+      R[b] = bv * (vv - gv * R[b]);
+      OT[b] *= args.scale * gtw[CH + 16 * b + i16];
     }
     // The previous chunk's output rows leave here, after the next chunk's
     // DMA has been issued, so they do not queue ahead of it.
     if (prev_t0 >= 0) store_out(prev_t0, prev_L);
     __syncthreads();  // (D) the inverse, -A and P^T operands of every wave are in LDS
 
-    // -- state, part 2: two-level solve, output and state update
+    // -- state, part 2: block solve, output and state update
     {
-      uint4 rh, rl, u0h, u0l, u1h, u1l;
-      split8(R[0], R[1], rh, rl);
-      const f32x4 U0 = mma32x3(sm.ttab[0][0][lane], sm.ttab[0][1][lane], rh, rl, zero4());
-      const f32x4 U1 = mma32x3(sm.ttab[1][0][lane], sm.ttab[1][1][lane], rh, rl, zero4());
-      split8(U0, U1, u0h, u0l);
-      R[2] = mma32x3(sm.ttab[4][0][lane], sm.ttab[4][1][lane], u0h, u0l, R[2]);
-      R[3] = mma32x3(sm.ttab[5][0][lane], sm.ttab[5][1][lane], u0h, u0l, R[3]);
-      split8(R[2], R[3], rh, rl);
-      const f32x4 U2 = mma32x3(sm.ttab[2][0][lane], sm.ttab[2][1][lane], rh, rl, zero4());
-      const f32x4 U3 = mma32x3(sm.ttab[3][0][lane], sm.ttab[3][1][lane], rh, rl, zero4());
-      split8(U2, U3, u1h, u1l);
+      uint2 rh, rl, u0h, u0l, u1h, u1l;
+      split4(R[0], rh, rl);
+      const f32x4 U0 = mma16x3(sm.ttab[0][0][lane], sm.ttab[0][1][lane], rh, rl, zero4());
+      split4(U0, u0h, u0l);
+      R[1] = mma16x3(sm.ttab[2][0][lane], sm.ttab[2][1][lane], u0h, u0l, R[1]);
+      split4(R[1], rh, rl);
+      const f32x4 U1 = mma16x3(sm.ttab[1][0][lane], sm.ttab[1][1][lane], rh, rl, zero4());
+      split4(U1, u1h, u1l);
 
-      OT[0] = mma32(u0h, sm.ptab[0][lane], OT[0]);
-      OT[1] = mma32(u0h, sm.ptab[1][lane], OT[1]);
-      OT[2] = mma32(u0h, sm.ptab[2][lane], OT[2]);
-      OT[2] = mma32(u1h, sm.ptab[3][lane], OT[2]);
-      OT[3] = mma32(u0h, sm.ptab[4][lane], OT[3]);
-      OT[3] = mma32(u1h, sm.ptab[5][lane], OT[3]);
+      const uint4 uh = make_uint4(u0h.x, u0h.y, u1h.x, u1h.y);
+      OT[0] = mma32(uh, sm.ptab[0][lane], OT[0]);
+      OT[1] = mma32(uh, sm.ptab[1][lane], OT[1]);
 
-      uint4 w0h, w0l, w1h, w1l;
+      uint4 wh, wl;
       {
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&gtw[3 * CH + 0 + 4 * h4]);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&gtw[3 * CH + 4 * h4]);
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(&gtw[3 * CH + 16 + 4 * h4]);
-        const f32x4 d2 = *reinterpret_cast<const f32x4*>(&gtw[3 * CH + 32 + 4 * h4]);
-        const f32x4 d3 = *reinterpret_cast<const f32x4*>(&gtw[3 * CH + 48 + 4 * h4]);
-        split8(d0 * U0, d1 * U1, w0h, w0l);
-        split8(d2 * U2, d3 * U3, w1h, w1l);
+        split8(d0 * U0, d1 * U1, wh, wl);
       }
       const float gL = gtw[CH + CH - 1];
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const char* kt = Ks + 32 * (mt & 1);
         const uint2 k0 = ld_tr(kt, ko[mt >> 1]), k1 = ld_tr(kt + ROW16, ko[mt >> 1]);
-        const uint2 k2 = ld_tr(kt + 2 * ROW16, ko[mt >> 1]), k3 = ld_tr(kt + 3 * ROW16, ko[mt >> 1]);
-        const uint4 a0 = make_uint4(k0.x, k0.y, k1.x, k1.y), a1 = make_uint4(k2.x, k2.y, k3.x, k3.y);
+        const uint4 a = make_uint4(k0.x, k0.y, k1.x, k1.y);
         f32x4 acc = S[mt] * gL;
-        acc = mma32(a0, w0h, acc);
-        acc = mma32(a0, w0l, acc);
-        acc = mma32(a1, w1h, acc);
-        S[mt] = mma32(a1, w1l, acc);
+        acc = mma32(a, wh, acc);
+        S[mt] = mma32(a, wl, acc);
       }
+      // Stage this chunk's output: token 16b + i16, value columns col_w + 4h4..+3.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int li = ln & 15, lh = ln >> 4;
+      const int sto_w = li * 256 + 16 * ((2 * cw + (lh >> 1)) ^ li) + 8 * (lh & 1);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        *reinterpret_cast<uint2*>(sm.ost + sto_w + b * 16 * 256) = make_uint2(pk2(OT[b][0], OT[b][1]), pk2(OT[b][2], OT[b][3]));
+      for (int b = 0; b < 2; ++b)
+        *reinterpret_cast<uint2*>(sm.ost + sto_w + b * 16 * 256) =
+            make_uint2(pk2(OT[b][0], OT[b][1]), pk2(OT[b][2], OT[b][3]));
     }
     prev_t0 = t0;
     prev_L = Lc;
