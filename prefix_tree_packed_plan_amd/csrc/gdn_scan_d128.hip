@@ -65,6 +65,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2 lds_u2;
 
 constexpr int CH = 32;          // chunk length (tokens)
 constexpr int D = 128;          // d_k = d_v
@@ -135,11 +137,16 @@ __device__ __forceinline__ int toff(int row, int col) {
 // col0 + kmap(h, 0..7), kmap(h, j) = j<4 ? 4h+j : 16+4h+(j-4); the two 8-byte
 // pieces are 32 bytes apart in this layout.  The same K order lets two
 // accumulator tiles (rows 4h..4h+3 of each) serve as one K = 32 operand
-// without moving data.
+// without moving data.  The second address is hidden from the compiler so
+// that the pieces stay two ds_read_b64: fused into one ds_read2_b64 they
+// take several times as long on this part.
 __device__ __forceinline__ uint4 ld_a8(const char* t, int o) {
-  const uint2* p = reinterpret_cast<const uint2*>(t + o);
-  const uint2 x = p[0], y = p[4];
-  return make_uint4(x.x, x.y, y.x, y.y);
+  const lds_u2* p0 = (const lds_u2*)(t + o);
+  uint32_t a1 = static_cast<uint32_t>((uintptr_t)p0) + 32;
+  asm volatile("" : "+v"(a1));
+  const lds_u2* p1 = (const lds_u2*)(uintptr_t)a1;
+  const u32x2 x = *p0, y = *p1;
+  return make_uint4(x[0], x[1], y[0], y[1]);
 }
 // Transposing read at byte offset `o` = toff(row0 + 4h + i/4, col0 + 4(i%4))
 // for lane i of 16-lane group h: the lane gets rows row0 + 4h + 0..3 of
@@ -153,8 +160,9 @@ struct Smem {
   alignas(16) char kb[2][TSZ];       // K tiles
   alignas(16) char qb[2][TSZ];       // Q tiles
   alignas(16) char vb[2][TSZ];       // V tiles
-  // 16x16x16 A operands per lane, [hi, lo]: 0 = T_00, 1 = T_11, 2 = -A_10.
-  alignas(16) uint2 ttab[3][2][64];
+  // 16x16x16 A operands per lane, hi in .xy and lo in .zw: 0 = T_00,
+  // 1 = T_11, 2 = -A_10.
+  alignas(16) uint4 ttab[3][64];
   // 16x16x32 B operands of O^T += U^T P^T for token blocks 0 and 1.
   alignas(16) uint4 ptab[2][64];
   // Waves 0, 1: their gated diagonal block, A[r][4q + p] at [r][p][q].
@@ -376,14 +384,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         if ((rr & 3) == ph) t[rr >> 2] = val;
       }
       // T[4q + ph][jc] -> operand lane (row 4q + ph, group jc / 4), element jc % 4.
-      uint16_t* th = reinterpret_cast<uint16_t*>(&sm.ttab[cw][0][0]);
-      uint16_t* tl = reinterpret_cast<uint16_t*>(&sm.ttab[cw][1][0]);
+      uint16_t* tt = reinterpret_cast<uint16_t*>(&sm.ttab[cw][0]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int e = (4 * q + ph + 16 * (jc >> 2)) * 4 + (jc & 3);
+        const int e = (4 * q + ph + 16 * (jc >> 2)) * 8 + (jc & 3);
         const uint32_t w = pk2(t[q], 0.f);
-        th[e] = static_cast<uint16_t>(w);
-        tl[e] = static_cast<uint16_t>(pk2(t[q] - lo_f(w), 0.f));
+        tt[e] = static_cast<uint16_t>(w);
+        tt[e + 4] = static_cast<uint16_t>(pk2(t[q] - lo_f(w), 0.f));
       }
     } else if (cw == 2) {
       // -A_10 as the A operand of R_1 -= A_10 U_0: lane i (token 16 + i),
@@ -397,8 +404,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       for (int r = 0; r < 4; ++r) v[r] = -bi * d[r] * ex2(gi - gj[r]);
       uint2 vh, vl;
       split4(v, vh, vl);
-      sm.ttab[2][0][lane] = vh;
-      sm.ttab[2][1][lane] = vl;
+      sm.ttab[2][lane] = make_uint4(vh.x, vh.y, vl.x, vl.y);
     } else if (cw == 3 || cw >= 6) {
       // P^T block (jb, ib) = (0, 0), (0, 1), (1, 1): lane i (query), rows j (key).
       const int jb = cw == 7 ? 1 : 0, ib = cw == 3 ? 0 : 1;
@@ -446,12 +452,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     // -- state, part 2: block solve, output and state update
     {
       uint2 rh, rl, u0h, u0l, u1h, u1l;
+      const uint4 t0 = sm.ttab[0][lane], t1 = sm.ttab[1][lane], na = sm.ttab[2][lane];
       split4(R[0], rh, rl);
-      const f32x4 U0 = mma16x3(sm.ttab[0][0][lane], sm.ttab[0][1][lane], rh, rl, zero4());
+      const f32x4 U0 = mma16x3(make_uint2(t0.x, t0.y), make_uint2(t0.z, t0.w), rh, rl, zero4());
       split4(U0, u0h, u0l);
-      R[1] = mma16x3(sm.ttab[2][0][lane], sm.ttab[2][1][lane], u0h, u0l, R[1]);
+      R[1] = mma16x3(make_uint2(na.x, na.y), make_uint2(na.z, na.w), u0h, u0l, R[1]);
       split4(R[1], rh, rl);
-      const f32x4 U1 = mma16x3(sm.ttab[1][0][lane], sm.ttab[1][1][lane], rh, rl, zero4());
+      const f32x4 U1 = mma16x3(make_uint2(t1.x, t1.y), make_uint2(t1.z, t1.w), rh, rl, zero4());
       split4(U1, u1h, u1l);
 
       const uint4 uh = make_uint4(u0h.x, u0h.y, u1h.x, u1h.y);
