@@ -369,9 +369,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
           arow[rr][0] = v.x, arow[rr][1] = v.y, arow[rr][2] = v.z, arow[rr][3] = v.w;
         }
       }
-      float t[4];
+      // T[r][jc] = delta(r, jc) - sum_{m<r} A[r][m] T[m][jc] for every r:
+      // starting from the identity, rows above the diagonal stay zero by
+      // themselves.  Lane phase ph owns rows r = 4q + ph; w[p] = (p == ph)
+      // selects the lanes that own row r.
+      float t[4], w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) t[q] = 4 * q + ph == jc ? 1.f : 0.f;
+      for (int q = 0; q < 4; ++q) {
+        t[q] = 4 * q + ph == jc ? 1.f : 0.f;
+        w[q] = q == ph ? 1.f : 0.f;
+      }
 #pragma unroll
       for (int rr = 1; rr < 16; ++rr) {
         // A is strictly lower (zeros from the gated tile), so terms with
@@ -379,9 +386,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         float part = 0.f;
 #pragma unroll
         for (int q = 0; 4 * q < rr; ++q) part += arow[rr][q] * t[q];
-        const float sum = quad_sum(part);
-        const float val = rr > jc ? -sum : (rr == jc ? 1.f : 0.f);
-        if ((rr & 3) == ph) t[rr >> 2] = val;
+        t[rr >> 2] -= w[rr & 3] * quad_sum(part);
       }
       // T[4q + ph][jc] -> operand lane (row 4q + ph, group jc / 4), element jc % 4.
       uint16_t* tt = reinterpret_cast<uint16_t*>(&sm.ttab[cw][0]);
