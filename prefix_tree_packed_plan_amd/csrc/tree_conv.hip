@@ -25,7 +25,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 64;   // tokens per thread
-constexpr int kBatch = 8;   // loads issued together
+constexpr int kBatch = 4;   // loads issued together (8 measured slower: fewer waves fit)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -34,10 +34,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Rows are touched once (the W-1 rows re-read at tile starts aside), so the
+// 16-byte accesses are non-temporal.
 template <typename T, int VEC>
 __device__ __forceinline__ void load_row(const T* __restrict__ p, float (&out)[VEC]) {
   if constexpr (sizeof(T) * VEC == 16) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const uint4 raw = make_uint4(v[0], v[1], v[2], v[3]);
     if constexpr (sizeof(T) == 2) {
       const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -77,7 +82,7 @@ __device__ __forceinline__ void store_row(T* __restrict__ p, const float (&in)[V
       raw = make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
                        __float_as_uint(in[3]));
     }
-    *reinterpret_cast<uint4*>(p) = raw;
+    __builtin_nontemporal_store(u32x4{raw.x, raw.y, raw.z, raw.w}, reinterpret_cast<u32x4*>(p));
   } else {
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
