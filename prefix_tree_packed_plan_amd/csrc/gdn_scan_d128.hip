@@ -426,12 +426,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
 
     // -- state, part 1: R = diag(b)(V - gamma K S0), O^T = scale gamma (S0^T Q^T)
+    // S is decayed by gamma_L for the update of part 2 as soon as each pair
+    // of tiles has been split, far ahead of the MFMAs that accumulate into it.
+    const float gL = gtw[CH + CH - 1];
     f32x4 R[2], OT[2];
     R[0] = R[1] = OT[0] = OT[1] = zero4();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint4 sh, sl;
       split8(S[2 * kk], S[2 * kk + 1], sh, sl);
+      S[2 * kk] *= gL;
+      S[2 * kk + 1] *= gL;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const uint4 ak = ld_a8(Ks + ROW16 * b, ao[kk]);
@@ -476,15 +481,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(&gtw[3 * CH + 16 + 4 * h4]);
         split8(d0 * U0, d1 * U1, wh, wl);
       }
-      const float gL = gtw[CH + CH - 1];
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const char* kt = Ks + 32 * (mt & 1);
         const uint2 k0 = ld_tr(kt, ko[mt >> 1]), k1 = ld_tr(kt + ROW16, ko[mt >> 1]);
         const uint4 a = make_uint4(k0.x, k0.y, k1.x, k1.y);
-        f32x4 acc = S[mt] * gL;
-        acc = mma32(a, wh, acc);
-        S[mt] = mma32(a, wl, acc);
+        S[mt] = mma32(a, wh, S[mt]);
+        S[mt] = mma32(a, wl, S[mt]);
       }
       // Stage this chunk's output: token 16b + i16, value columns col_w + 4h4..+3.
       int ln = lane;
