@@ -136,22 +136,32 @@ int tree_plan_upload(const tree_plan_t* plan, void* dplan, size_t dplan_bytes, v
  *
  *   y[t, c] = act( sum_{i=0}^{W-1} w[c, i] * xin(t, i - (W-1), c) + bias[c] )
  *
- * where xin(t, -j, c) is the input j steps back along t's root path (zero
- * before the root); w[c, W-1] multiplies token t itself.
+ * with w[c, W-1] multiplying token t itself,
+ * where xin(t, -j, c) is the input j steps back along t's root path; before
+ * the root it is the root's context row (init_ctx) or zero.
  *
- * x     device, [n_tokens, channels], dtype           (read)
- * w     device, [channels, W], dtype                  (read)
- * bias  device, [channels], dtype, or NULL            (read)
- * y     device, [n_tokens, channels], dtype           (written; must not alias x)
+ * x        device, [n_tokens, channels], dtype        (read)
+ * w        device, [channels, W], dtype               (read)
+ * bias     device, [channels], dtype, or NULL         (read)
+ * y        device, [n_tokens, channels], dtype        (written; must not alias x)
+ * init_ctx device, [n_roots, W-1, channels], dtype, or NULL: for the r-th
+ *          root in segment order, the W-1 inputs in front of it, oldest
+ *          first -- the conv state a partition gateway hands over across a
+ *          cut ("Tree Training" section 3.3 and appendix B.7).  NULL = zeros.
+ *                                                     (read)
+ * ctx_out  device, [n_seg, W-1, channels], dtype, or NULL: for every
+ *          segment, the W-1 path inputs ending at its last token, oldest
+ *          first (the conv state a child, or the next partition, continues
+ *          from).  Ignored when W = 1.                (written)
  * dtype TREE_DTYPE_F32 or TREE_DTYPE_BF16; arithmetic in fp32.
  * act   TREE_ACT_NONE or TREE_ACT_SILU (y = z * sigmoid(z)).
  * dplan device copy of `plan` made by tree_plan_upload.
  * Errors: INVALID_ARG, SIZE (n_tokens != plan N), UNSUPPORTED (W > 4),
  * HIP.
  */
-int tree_conv(const void* x, const void* w, const void* bias, void* y, int64_t n_tokens,
-              int32_t channels, int32_t dtype, int32_t act, const tree_plan_t* plan,
-              const void* dplan, void* stream);
+int tree_conv(const void* x, const void* w, const void* bias, void* y, const void* init_ctx,
+              void* ctx_out, int64_t n_tokens, int32_t channels, int32_t dtype, int32_t act,
+              const tree_plan_t* plan, const void* dplan, void* stream);
 
 /*
  * tree_scan_workspace_bytes -- device workspace tree_gdn_scan needs: one fp32
@@ -171,6 +181,9 @@ size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d
  *        keeps every exponent the kernel forms non-positive       (read)
  * beta   device, [n_tokens, h_v], fp32                 (read)
  * o      device, [n_tokens, h_v, d_v], dtype           (written)
+ * init_states device, [n_roots, h_v, d_k, d_v] fp32, or NULL: the state the
+ *        r-th root (in segment order) starts from, as a partition gateway
+ *        hands it over ("Tree Training" appendix B.7).  NULL = zero.  (read)
  * states device, [n_seg, h_v, d_k, d_v] fp32, or NULL: every segment's
  *        state after its last token, [d_k, d_v] orientation (the appendix's
  *        state tensor).  When given, children read their parents' states
@@ -186,7 +199,8 @@ size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d
  * Errors: INVALID_ARG, SIZE, UNSUPPORTED, WORKSPACE, HIP.
  */
 int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g,
-                  const float* beta, void* o, float* states, int64_t n_tokens, int32_t h_qk,
+                  const float* beta, void* o, const float* init_states, float* states,
+                  int64_t n_tokens, int32_t h_qk,
                   int32_t h_v, int32_t d_k, int32_t d_v, float scale, int32_t dtype,
                   int32_t sched, const tree_plan_t* plan, const void* dplan, void* ws,
                   size_t ws_bytes, void* stream);

@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .trie import check_trie, leaf_paths, path_token_index, root_path, segment_offsets
+from .trie import check_trie, leaf_paths, path_token_index, root_path, roots_of, segment_offsets
 
 
 def _token_step(S, a, b, kt, vt, qt, scale):
@@ -69,14 +69,17 @@ def gdn_on_path(q, k, v, g, beta, scale=1.0, snap_at=(), heads=None,
 
 
 def tree_gdn_reference(parents, seg_lens, q, k, v, g, beta, scale=1.0,
-                       segments=None, heads=None, dtype=np.float64):
+                       segments=None, heads=None, dtype=np.float64, init_states=None):
     """Per-path gated delta rule over the packed trie.
 
     Returns (o [N, H_v, d_v], states [n_seg, H_v, d_k, d_v]) in `dtype`,
-    NaN where not computed.  With segments=None every root-to-leaf path is
-    run and a segment shared by several paths must come out bitwise
-    identical from each (Eq. 6).  With a list of segments only the root
-    paths of those segments are run; `heads` restricts the value heads.
+    NaN where not computed.  init_states [n_roots, H_v, d_k, d_v]: the
+    state each root starts from (roots in segment order; default zero; a
+    partition gateway hands it across a cut, appendix B.7).  With
+    segments=None every root-to-leaf path is run and a segment shared by
+    several paths must come out bitwise identical from each (Eq. 6).  With
+    a list of segments only the root paths of those segments are run;
+    `heads` restricts the value heads.
     """
     parents, seg_lens = check_trie(parents, seg_lens)
     q = np.asarray(q)
@@ -85,6 +88,7 @@ def tree_gdn_reference(parents, seg_lens, q, k, v, g, beta, scale=1.0,
     n = int(np.sum(seg_lens))
     heads = np.arange(h_v) if heads is None else np.asarray(heads, dtype=np.int64)
     off = segment_offsets(seg_lens)
+    rank = {r: i for i, r in enumerate(roots_of(parents))}
     o = np.full((n, h_v, d_v), np.nan, dtype=dtype)
     st = np.full((len(parents), h_v, d_k, d_v), np.nan, dtype=dtype)
     done = np.zeros(len(parents), dtype=bool)
@@ -95,8 +99,9 @@ def tree_gdn_reference(parents, seg_lens, q, k, v, g, beta, scale=1.0,
         for s in path:
             pos += int(seg_lens[s])
             ends.append(pos - 1)
+        init = None if init_states is None else np.asarray(init_states)[rank[path[0]]][heads]
         op, snaps = gdn_on_path(q[idx], k[idx], v[idx], g[idx], beta[idx], scale,
-                                snap_at=ends, heads=heads, dtype=dtype)
+                                snap_at=ends, heads=heads, init=init, dtype=dtype)
         pos = 0
         for s, e in zip(path, ends):
             m = int(seg_lens[s])

@@ -49,6 +49,11 @@ def children_of(parents):
     return kids
 
 
+def roots_of(parents):
+    """Roots in segment order (the order initial states and contexts use)."""
+    return [i for i, p in enumerate(parents) if int(p) < 0]
+
+
 def leaves_of(parents):
     kids = children_of(parents)
     return [i for i in range(len(parents)) if not kids[i]]

@@ -56,9 +56,9 @@ SIGNATURES = {
     "tree_plan_levels": (ctypes.c_int, [_P, _P, _P]),
     "tree_plan_device_bytes": (_SZ, [_P]),
     "tree_plan_upload": (ctypes.c_int, [_P, _P, _SZ, _P]),
-    "tree_conv": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]),
+    "tree_conv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]),
     "tree_scan_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
-    "tree_gdn_scan": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
+    "tree_gdn_scan": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
                                      _F, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "tree_last_error": (ctypes.c_char_p, []),
 }
@@ -134,6 +134,10 @@ class TreePlan:
     def conv_width(self) -> int:
         return int(self.stats["conv_width"])
 
+    @property
+    def n_roots(self) -> int:
+        return int(self.stats["n_roots"])
+
     def conv_history(self) -> np.ndarray:
         w1 = self.conv_width - 1
         out = np.zeros((self.n_seg, max(w1, 0)), np.int32)
@@ -199,8 +203,13 @@ def _need(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def tree_conv(x, w, plan: TreePlan, bias=None, act: Optional[str] = None, out=None):
-    """y = tree-aware causal depthwise conv of x [N, C] with w [C, W]."""
+def tree_conv(x, w, plan: TreePlan, bias=None, act: Optional[str] = None, out=None,
+              init_ctx=None, return_ctx: bool = False, ctx_out=None):
+    """y = tree-aware causal depthwise conv of x [N, C] with w [C, W].
+
+    init_ctx [n_roots, W-1, C]: the inputs in front of each root (default
+    zeros).  With return_ctx (or ctx_out given) also returns the W-1 path
+    inputs ending at each segment's last token, [n_seg, W-1, C]."""
     import torch
     _need(x, "x")
     _need(w, "w", x.dtype, x.device)
@@ -208,20 +217,37 @@ def tree_conv(x, w, plan: TreePlan, bias=None, act: Optional[str] = None, out=No
         _need(bias, "bias", x.dtype, x.device)
     if x.dim() != 2 or w.dim() != 2 or w.shape[0] != x.shape[1] or w.shape[1] != plan.conv_width:
         raise ValueError("shapes must be x [N, C], w [C, W] with W = plan conv width")
+    w1 = plan.conv_width - 1
+    if init_ctx is not None:
+        _need(init_ctx, "init_ctx", x.dtype, x.device)
+        if tuple(init_ctx.shape) != (plan.n_roots, w1, x.shape[1]):
+            raise ValueError("init_ctx must be [n_roots, W-1, C]")
+    if return_ctx and ctx_out is None:
+        ctx_out = torch.empty((plan.n_seg, w1, x.shape[1]), dtype=x.dtype, device=x.device)
+    if ctx_out is not None:
+        _need(ctx_out, "ctx_out", x.dtype, x.device)
+        if tuple(ctx_out.shape) != (plan.n_seg, w1, x.shape[1]):
+            raise ValueError("ctx_out must be [n_seg, W-1, C]")
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", x.dtype, x.device)
     a = {None: ACT_NONE, "none": ACT_NONE, "silu": ACT_SILU, "swish": ACT_SILU}[act]
     dplan = plan.on_device(x.device)
     stream = torch.cuda.current_stream(x.device).cuda_stream
     _check(load().tree_conv(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
-                            y.data_ptr(), x.shape[0], x.shape[1], _dtype_code(x), a, plan.handle,
-                            dplan.data_ptr(), stream))
+                            y.data_ptr(), init_ctx.data_ptr() if init_ctx is not None else None,
+                            ctx_out.data_ptr() if ctx_out is not None else None,
+                            x.shape[0], x.shape[1], _dtype_code(x), a, plan.handle, dplan.data_ptr(), stream))
+    if return_ctx:
+        return y, ctx_out
     return y
 
 
 def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_states: bool = False,
-                  out=None, states=None, workspace=None):
-    """Tree gated delta rule: o [N, H_v, d_v] (and states [n_seg, H_v, d_k, d_v] fp32)."""
+                  out=None, states=None, workspace=None, init_states=None):
+    """Tree gated delta rule: o [N, H_v, d_v] (and states [n_seg, H_v, d_k, d_v] fp32).
+
+    init_states [n_roots, H_v, d_k, d_v] fp32: the states the roots start
+    from (default zero)."""
     import torch
     _need(q, "q")
     dev = q.device
@@ -241,6 +267,10 @@ def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_s
         states = torch.empty((plan.n_seg, h_v, d_k, d_v), dtype=torch.float32, device=dev)
     if states is not None:
         _need(states, "states", torch.float32, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", torch.float32, dev)
+        if tuple(init_states.shape) != (plan.n_roots, h_v, d_k, d_v):
+            raise ValueError("init_states must be [n_roots, H_v, d_k, d_v]")
     lib = load()
     need = int(lib.tree_scan_workspace_bytes(plan.handle, h_v, d_k, d_v, int(states is not None)))
     if need > 0 and (workspace is None or workspace.numel() < need):
@@ -248,7 +278,8 @@ def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_s
     dplan = plan.on_device(dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     _check(lib.tree_gdn_scan(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
-                             o.data_ptr(), states.data_ptr() if states is not None else None,
+                             o.data_ptr(), init_states.data_ptr() if init_states is not None else None,
+                             states.data_ptr() if states is not None else None,
                              n, h_qk, h_v, d_k, d_v, float(scale), _dtype_code(q), SCHED_LEVEL,
                              plan.handle, dplan.data_ptr(),
                              workspace.data_ptr() if workspace is not None else None,

@@ -101,9 +101,9 @@ int tree_plan_upload(const tree_plan_t* plan, void* dplan, size_t dplan_bytes, v
   return TREE_OK;
 }
 
-int tree_conv(const void* x, const void* w, const void* bias, void* y, int64_t n_tokens,
-              int32_t channels, int32_t dtype, int32_t act, const tree_plan_t* plan,
-              const void* dplan, void* stream) {
+int tree_conv(const void* x, const void* w, const void* bias, void* y, const void* init_ctx,
+              void* ctx_out, int64_t n_tokens, int32_t channels, int32_t dtype, int32_t act,
+              const tree_plan_t* plan, const void* dplan, void* stream) {
   if (!plan || !x || !w || !y || !dplan) return fail(TREE_ERR_INVALID_ARG, "tree_conv: null argument");
   const tg::Plan& p = plan->p;
   if (n_tokens != p.n_tokens)
@@ -115,9 +115,11 @@ int tree_conv(const void* x, const void* w, const void* bias, void* y, int64_t n
     return fail(TREE_ERR_INVALID_ARG, "tree_conv: bad activation %d", act);
   if (p.width > 4) return fail(TREE_ERR_UNSUPPORTED, "tree_conv: conv width %d > 4", p.width);
   if (x == y) return fail(TREE_ERR_INVALID_ARG, "tree_conv: y must not alias x");
+  if (ctx_out != nullptr && (ctx_out == x || ctx_out == y || ctx_out == init_ctx))
+    return fail(TREE_ERR_INVALID_ARG, "tree_conv: ctx_out must not alias x, y or init_ctx");
   const int32_t* base = static_cast<const int32_t*>(dplan);
   tg::ConvArgs a{x, w, bias, y, static_cast<int32_t>(n_tokens), channels, p.width, dtype, act,
-                 base + p.m_seg_off, base + p.m_hist, p.n_seg};
+                 base + p.m_seg_off, base + p.m_hist, p.n_seg, init_ctx, ctx_out, base + p.m_ctx};
   const hipError_t e = tg::launch_conv(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("tree_conv: launch", e);
   return TREE_OK;
@@ -130,9 +132,9 @@ size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d
 }
 
 int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                  void* o, float* states, int64_t n_tokens, int32_t h_qk, int32_t h_v, int32_t d_k,
-                  int32_t d_v, float scale, int32_t dtype, int32_t sched, const tree_plan_t* plan,
-                  const void* dplan, void* ws, size_t ws_bytes, void* stream) {
+                  void* o, const float* init_states, float* states, int64_t n_tokens, int32_t h_qk,
+                  int32_t h_v, int32_t d_k, int32_t d_v, float scale, int32_t dtype, int32_t sched,
+                  const tree_plan_t* plan, const void* dplan, void* ws, size_t ws_bytes, void* stream) {
   if (!plan || !q || !k || !v || !g || !beta || !o || !dplan)
     return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: null argument");
   const tg::Plan& p = plan->p;
@@ -160,6 +162,8 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, c
   a.g = g;
   a.beta = beta;
   a.o = o;
+  a.init = init_states;
+  a.root_idx = base + p.m_root;
   a.states = states;
   a.slots = static_cast<float*>(ws);
   a.seg_off = base + p.m_seg_off;

@@ -199,6 +199,8 @@ __global__ __launch_bounds__(64 * G * (DV / 32)) void gdn_level_kernel(ScanArgs 
     if (par >= 0)
       src = args.states ? args.states + (static_cast<size_t>(par) * args.h_v + h) * head_elems
                         : args.slots + (static_cast<size_t>(args.slot[par]) * args.h_v + h) * head_elems;
+    else if (args.init)  // a root with a caller-given initial state
+      src = args.init + (static_cast<size_t>(args.root_idx[seg]) * args.h_v + h) * head_elems;
     if (src) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)

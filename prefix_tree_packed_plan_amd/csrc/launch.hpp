@@ -20,6 +20,9 @@ struct ConvArgs {
   const int32_t* seg_off;  // device, n_seg + 1
   const int32_t* hist;     // device, n_seg * (width - 1)
   int32_t n_seg;
+  const void* init_ctx;    // [n_roots, width - 1, channels] or null (zeros)
+  void* ctx_out;           // [n_seg, width - 1, channels] or null
+  const int32_t* ctx_src;  // device, n_seg * (width - 1)
 };
 
 // Returns hipSuccess or the launch error.
@@ -32,6 +35,8 @@ struct ScanArgs {
   const float* g;
   const float* beta;
   void* o;
+  const float* init;  // [n_roots, h_v, d_k, d_v] initial states of the roots, or null (zeros)
+  const int32_t* root_idx;  // root rank of each segment, -1 for a non-root
   float* states;  // [n_seg, h_v, d_k, d_v] or null
   float* slots;   // [n_parents, h_v, d_k, d_v] when states is null
   const int32_t* seg_off;

@@ -98,19 +98,35 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   for (int32_t i = 0; i < n_seg; ++i) p.level_start[p.depth[i] + 1] += 1;
   for (int32_t l = 0; l < p.n_levels; ++l) p.level_start[l + 1] += p.level_start[l];
 
-  // Conv history: the W-1 packed rows preceding segment i on its path are the
-  // last W-1 entries of (hist[parent] ++ rows of parent); -1 pads at a root.
+  // Roots in segment order.
+  p.root_idx.assign(n_seg, -1);
+  for (int32_t i = 0, r = 0; i < n_seg; ++i)
+    if (p.parents[i] < 0) p.root_idx[i] = r++;
+
+  // Conv history: the W-1 rows preceding segment i on its path are the last
+  // W-1 entries of (hist[parent] ++ rows of parent); a root's are its
+  // context positions -1 - (r (W-1) + j).  ctx_src[i] is the same for the
+  // W-1 rows ending at segment i's last token: the last W-1 entries of
+  // (hist[i] ++ rows of i).
   const int32_t H = conv_width - 1;
   p.hist.assign(static_cast<size_t>(n_seg) * H, -1);
+  p.ctx_src.assign(static_cast<size_t>(n_seg) * H, -1);
   std::vector<int32_t> ext;
+  auto tail = [&](int32_t s, int32_t* dst) {  // last H of (hist[s] ++ rows of s)
+    ext.assign(p.hist.begin() + static_cast<size_t>(s) * H, p.hist.begin() + static_cast<size_t>(s + 1) * H);
+    const int32_t take = std::min(p.lens[s], H);
+    for (int32_t j = p.lens[s] - take; j < p.lens[s]; ++j) ext.push_back(p.seg_off[s] + j);
+    std::copy(ext.end() - H, ext.end(), dst);
+  };
   for (int32_t i = 0; i < n_seg && H > 0; ++i) {
     const int32_t par = p.parents[i];
-    if (par < 0) continue;
-    ext.assign(p.hist.begin() + static_cast<size_t>(par) * H,
-               p.hist.begin() + static_cast<size_t>(par + 1) * H);
-    const int32_t take = std::min(p.lens[par], H);
-    for (int32_t j = p.lens[par] - take; j < p.lens[par]; ++j) ext.push_back(p.seg_off[par] + j);
-    std::copy(ext.end() - H, ext.end(), p.hist.begin() + static_cast<size_t>(i) * H);
+    int32_t* hi = p.hist.data() + static_cast<size_t>(i) * H;
+    if (par < 0) {
+      for (int32_t j = 0; j < H; ++j) hi[j] = -1 - (p.root_idx[i] * H + j);
+    } else {
+      tail(par, hi);
+    }
+    tail(i, p.ctx_src.data() + static_cast<size_t>(i) * H);
   }
 
   // Device mirror.
@@ -119,12 +135,16 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   p.m_slot = p.m_parent + n_seg;
   p.m_hist = p.m_slot + n_seg;
   p.m_order = p.m_hist + p.hist.size();
-  p.mirror.resize(p.m_order + n_seg);
+  p.m_root = p.m_order + n_seg;
+  p.m_ctx = p.m_root + n_seg;
+  p.mirror.resize(p.m_ctx + p.ctx_src.size());
   std::copy(p.seg_off.begin(), p.seg_off.end(), p.mirror.begin() + p.m_seg_off);
   std::copy(p.parents.begin(), p.parents.end(), p.mirror.begin() + p.m_parent);
   std::copy(p.slot.begin(), p.slot.end(), p.mirror.begin() + p.m_slot);
   std::copy(p.hist.begin(), p.hist.end(), p.mirror.begin() + p.m_hist);
   std::copy(p.order.begin(), p.order.end(), p.mirror.begin() + p.m_order);
+  std::copy(p.root_idx.begin(), p.root_idx.end(), p.mirror.begin() + p.m_root);
+  std::copy(p.ctx_src.begin(), p.ctx_src.end(), p.mirror.begin() + p.m_ctx);
 
   *out = std::move(p);
   return TREE_OK;

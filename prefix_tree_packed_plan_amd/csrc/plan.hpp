@@ -7,6 +7,11 @@
 // parent's final state ("Tree Training" section 3.2, Eq. 10: parents precede
 // children), and the conv history table that gives each segment the last
 // W-1 inputs of its own path (section 3.2, Eq. 11).
+//
+// History entries: h >= 0 is a packed token row; h < 0 is position
+// -1 - h of the roots' caller-given contexts (root r, context row j, oldest
+// first: code -1 - (r (W-1) + j)), which read as zeros when no context is
+// given.
 #pragma once
 
 #include <cstddef>
@@ -24,12 +29,16 @@ struct Plan {
   int64_t path_tokens = 0, max_path_tokens = 0;
 
   std::vector<int32_t> parents, lens, seg_off, depth, slot, hist;
+  // root_idx[s]: rank of root s among the roots in segment order, -1 for a
+  // non-root.  ctx_src[s][j]: source of the j-th (oldest first) of the W-1
+  // path inputs ending at segment s's last token, coded like hist.
+  std::vector<int32_t> root_idx, ctx_src;
   std::vector<int32_t> level_start;  // n_levels + 1
   std::vector<int32_t> order;        // segments by (level, length desc, index)
 
   // Device copy: one int32 array; element offsets of each table inside it.
   std::vector<int32_t> mirror;
-  size_t m_seg_off = 0, m_parent = 0, m_slot = 0, m_hist = 0, m_order = 0;
+  size_t m_seg_off = 0, m_parent = 0, m_slot = 0, m_hist = 0, m_order = 0, m_root = 0, m_ctx = 0;
 
   size_t device_bytes() const { return mirror.size() * sizeof(int32_t); }
 };

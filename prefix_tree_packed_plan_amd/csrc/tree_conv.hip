@@ -13,8 +13,10 @@
 // own consecutive 16-byte chunks of one token row, so every load and store of
 // a wavefront covers 1 KiB of contiguous memory.  At a segment start the
 // window is refilled from the plan's history table (the packed rows of the
-// W-1 path tokens before the segment, -1 = zero), which also covers
-// ancestors shorter than W-1.
+// W-1 path tokens before the segment), which also covers ancestors shorter
+// than W-1.  Before a root the history names rows of the caller's root
+// contexts, or zeros when none are given (the partition gateway of the
+// same paper, appendix B.7: a cut hands the next partition its conv state).
 #include <hip/hip_runtime.h>
 
 #include "../../include/tree_gdn.h"
@@ -94,11 +96,26 @@ __device__ __forceinline__ void store_row(T* __restrict__ p, const float (&in)[V
   }
 }
 
+// Row `src` of the path history: a packed input row (src >= 0), row -1 - src
+// of the root contexts, or zeros when no contexts are given.
+template <typename T, int VEC>
+__device__ __forceinline__ void load_hist(const T* __restrict__ x, const T* __restrict__ ctx, int32_t src,
+                                          int32_t C, int32_t c0, float (&out)[VEC]) {
+  if (src >= 0) {
+    load_row<T, VEC>(x + static_cast<int64_t>(src) * C + c0, out);
+  } else if (ctx != nullptr) {
+    load_row<T, VEC>(ctx + static_cast<int64_t>(-1 - src) * C + c0, out);
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) out[e] = 0.f;
+  }
+}
+
 template <typename T, int VEC, int W>
 __global__ __launch_bounds__(kThreads) void tree_conv_kernel(
     const T* __restrict__ x, const T* __restrict__ w, const T* __restrict__ bias,
     T* __restrict__ y, int32_t n_tok, int32_t C, const int32_t* __restrict__ seg_off,
-    const int32_t* __restrict__ hist, int32_t n_seg, int32_t act) {
+    const int32_t* __restrict__ hist, int32_t n_seg, int32_t act, const T* __restrict__ ctx) {
   const int32_t c0 = (blockIdx.x * kThreads + threadIdx.x) * VEC;
   if (c0 >= C) return;
   const int32_t t0 = blockIdx.y * kTile;
@@ -146,12 +163,7 @@ __global__ __launch_bounds__(kThreads) void tree_conv_kernel(
     const int32_t back = j + 1;
     const int32_t pos = t0 - seg_start - back;  // path position relative to the segment
     const int32_t src = pos >= 0 ? t0 - back : hist[static_cast<int64_t>(s) * H + H + pos];
-    if (src >= 0) {
-      load_row<T, VEC>(x + static_cast<int64_t>(src) * C + c0, win[j]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) win[j][e] = 0.f;
-    }
+    load_hist<T, VEC>(x, ctx, src, C, c0, win[j]);
   }
 
   for (int32_t tb = t0; tb < t1; tb += kBatch) {
@@ -169,15 +181,8 @@ __global__ __launch_bounds__(kThreads) void tree_conv_kernel(
         seg_start = next_start;
         next_start = seg_off[s + 1];
 #pragma unroll
-        for (int j = 0; j < H; ++j) {
-          const int32_t src = hist[static_cast<int64_t>(s) * H + H - 1 - j];
-          if (src >= 0) {
-            load_row<T, VEC>(x + static_cast<int64_t>(src) * C + c0, win[j]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) win[j][e] = 0.f;
-          }
-        }
+        for (int j = 0; j < H; ++j)
+          load_hist<T, VEC>(x, ctx, hist[static_cast<int64_t>(s) * H + H - 1 - j], C, c0, win[j]);
       }
       float out[VEC];
 #pragma unroll
@@ -201,6 +206,20 @@ __global__ __launch_bounds__(kThreads) void tree_conv_kernel(
   }
 }
 
+// Conv context out: row (s, j) of ctx_out is history row ctx_src[s][j] (the
+// W-1 path inputs ending at segment s's last token, oldest first).
+template <typename T, int VEC>
+__global__ __launch_bounds__(kThreads) void conv_context_kernel(const T* __restrict__ x, const T* __restrict__ ctx,
+                                                                T* __restrict__ out, int32_t C,
+                                                                const int32_t* __restrict__ ctx_src) {
+  const int32_t c0 = (blockIdx.x * kThreads + threadIdx.x) * VEC;
+  if (c0 >= C) return;
+  const int64_t row = blockIdx.y;  // s (W-1) + j
+  float v[VEC];
+  load_hist<T, VEC>(x, ctx, ctx_src[row], C, c0, v);
+  store_row<T, VEC>(out + row * C + c0, v);
+}
+
 template <typename T, int VEC>
 hipError_t launch_w(const ConvArgs& a, hipStream_t stream) {
   const int32_t nvec = (a.channels + VEC - 1) / VEC;
@@ -209,13 +228,18 @@ hipError_t launch_w(const ConvArgs& a, hipStream_t stream) {
   const T* w = static_cast<const T*>(a.w);
   const T* b = static_cast<const T*>(a.bias);
   T* y = static_cast<T*>(a.y);
+  const T* ctx = static_cast<const T*>(a.init_ctx);
   switch (a.width) {
-    case 1: tree_conv_kernel<T, VEC, 1><<<grid, kThreads, 0, stream>>>(x, w, b, y, a.n_tok, a.channels, a.seg_off, a.hist, a.n_seg, a.act); break;
-    case 2: tree_conv_kernel<T, VEC, 2><<<grid, kThreads, 0, stream>>>(x, w, b, y, a.n_tok, a.channels, a.seg_off, a.hist, a.n_seg, a.act); break;
-    case 3: tree_conv_kernel<T, VEC, 3><<<grid, kThreads, 0, stream>>>(x, w, b, y, a.n_tok, a.channels, a.seg_off, a.hist, a.n_seg, a.act); break;
-    case 4: tree_conv_kernel<T, VEC, 4><<<grid, kThreads, 0, stream>>>(x, w, b, y, a.n_tok, a.channels, a.seg_off, a.hist, a.n_seg, a.act); break;
+    case 1: tree_conv_kernel<T, VEC, 1><<<grid, kThreads, 0, stream>>>(x, w, b, y, a.n_tok, a.channels, a.seg_off, a.hist, a.n_seg, a.act, ctx); break;
+    case 2: tree_conv_kernel<T, VEC, 2><<<grid, kThreads, 0, stream>>>(x, w, b, y, a.n_tok, a.channels, a.seg_off, a.hist, a.n_seg, a.act, ctx); break;
+    case 3: tree_conv_kernel<T, VEC, 3><<<grid, kThreads, 0, stream>>>(x, w, b, y, a.n_tok, a.channels, a.seg_off, a.hist, a.n_seg, a.act, ctx); break;
+    case 4: tree_conv_kernel<T, VEC, 4><<<grid, kThreads, 0, stream>>>(x, w, b, y, a.n_tok, a.channels, a.seg_off, a.hist, a.n_seg, a.act, ctx); break;
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ctx_out == nullptr || a.width < 2) return e;
+  dim3 cgrid(grid.x, static_cast<unsigned>(a.n_seg) * (a.width - 1));
+  conv_context_kernel<T, VEC><<<cgrid, kThreads, 0, stream>>>(x, ctx, static_cast<T*>(a.ctx_out), a.channels, a.ctx_src);
   return hipGetLastError();
 }
 
@@ -225,7 +249,8 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   const bool bf16 = a.dtype == TREE_DTYPE_BF16;
   const int vec = bf16 ? 8 : 4;
   const auto aligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-  const bool wide = (a.channels % vec == 0) && aligned(a.x) && aligned(a.y);
+  const bool wide = (a.channels % vec == 0) && aligned(a.x) && aligned(a.y) &&
+                    (a.init_ctx == nullptr || aligned(a.init_ctx)) && (a.ctx_out == nullptr || aligned(a.ctx_out));
   if (bf16) return wide ? launch_w<uint16_t, 8>(a, stream) : launch_w<uint16_t, 1>(a, stream);
   return wide ? launch_w<float, 4>(a, stream) : launch_w<float, 1>(a, stream);
 }

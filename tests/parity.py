@@ -68,11 +68,14 @@ def sample_segments(parents, lens, k, seed=0):
     return picks
 
 
-def scan_errors_full(parents, lens, q, k, v, g, beta, o_gpu, st_gpu, scale=1.0, heads=None):
+def scan_errors_full(parents, lens, q, k, v, g, beta, o_gpu, st_gpu, scale=1.0, heads=None,
+                     init_states=None):
     """Run the oracle on every path (optionally a head subset) and compare all
     rows / states.  Returns (max abs output error, max state rel error)."""
     tq, tk, tv, tg_, tb = (to_np(x) for x in (q, k, v, g, beta))
-    o_ref, s_ref = ogdn.tree_gdn_reference(parents, lens, tq, tk, tv, tg_, tb, scale, heads=heads)
+    init = None if init_states is None else to_np(init_states)
+    o_ref, s_ref = ogdn.tree_gdn_reference(parents, lens, tq, tk, tv, tg_, tb, scale, heads=heads,
+                                           init_states=init)
     hs = np.arange(tv.shape[1]) if heads is None else np.asarray(heads)
     sg = to_np(st_gpu)[:, hs]
     return out_err(o_gpu, o_ref[:, hs], cols=hs), float(state_rel_err(sg, s_ref[:, hs]).max())
@@ -97,7 +100,8 @@ def scan_errors_sampled(parents, lens, q, k, v, g, beta, o_gpu, st_gpu, segments
     return worst_o, worst_s
 
 
-def conv_errors(parents, lens, x, w, y_gpu, bias=None, act=None, segments=None, channels=None):
+def conv_errors(parents, lens, x, w, y_gpu, bias=None, act=None, segments=None, channels=None,
+                init_ctx=None):
     """Max abs error of the tree conv against the per-path oracle; with
     `segments`, only those segments' root paths (and `channels` subset)."""
     import torch
@@ -105,7 +109,8 @@ def conv_errors(parents, lens, x, w, y_gpu, bias=None, act=None, segments=None, 
     tw = to_np(w)[cs]
     tb = None if bias is None else to_np(bias)[cs]
     if segments is None:
-        ref = oconv.tree_conv_reference(parents, lens, to_np(x)[:, cs], tw, tb, act)
+        ctx = None if init_ctx is None else to_np(init_ctx)[:, :, cs]
+        ref = oconv.tree_conv_reference(parents, lens, to_np(x)[:, cs], tw, tb, act, init_ctx=ctx)
         return out_err(y_gpu, ref, cols=cs)
     worst = 0.0
     for s in segments:
@@ -114,3 +119,26 @@ def conv_errors(parents, lens, x, w, y_gpu, bias=None, act=None, segments=None, 
         yp = oconv.conv_on_path(to_np(x.index_select(0, idx))[:, cs], tw, tb, act)
         worst = max(worst, out_err(y_gpu.index_select(0, idx), yp, cols=cs))
     return worst
+
+
+def split_subtree(parents, c):
+    """Cut segment c's subtree out of a trie (host bookkeeping, no
+    arithmetic).  Returns (keep, parents_keep, index_keep, sub,
+    parents_sub, index_sub): the kept and cut segment lists in original
+    order, each with parents renumbered into its own list and a map
+    original -> new index; c becomes the root of the cut part."""
+    parents = [int(p) for p in parents]
+    sub = {c}
+    for i in range(c + 1, len(parents)):
+        if parents[i] in sub:
+            sub.add(i)
+    keep = [i for i in range(len(parents)) if i not in sub]
+    subl = sorted(sub)
+
+    def renumber(segs):
+        idx = {s: i for i, s in enumerate(segs)}
+        return np.array([idx.get(parents[s], -1) if s != c else -1 for s in segs], np.int32), idx
+
+    pa, ia = renumber(keep)
+    pb, ib = renumber(subl)
+    return keep, pa, ia, subl, pb, ib

@@ -62,14 +62,22 @@ def test_planted_gdn_mistake_is_caught(monkeypatch, bad):
     assert _fails(GDN_PINS)
 
 
-def _conv_taps_reversed(xp, w, bias=None, act=None, dtype=np.float64):
-    return ORIG_CONV(xp, np.asarray(w)[:, ::-1], bias, act, dtype)
+def _conv_taps_reversed(xp, w, bias=None, act=None, dtype=np.float64, ctx=None):
+    return ORIG_CONV(xp, np.asarray(w)[:, ::-1], bias, act, dtype, ctx=ctx)
 
 
-def _conv_no_padding_history(xp, w, bias=None, act=None, dtype=np.float64):
-    y = ORIG_CONV(xp, w, bias, act, dtype)
+def _conv_no_padding_history(xp, w, bias=None, act=None, dtype=np.float64, ctx=None):
+    y = ORIG_CONV(xp, w, bias, act, dtype, ctx=ctx)
     y[: w.shape[1] - 1] = 0.0
     return y
+
+
+def _conv_context_ignored(xp, w, bias=None, act=None, dtype=np.float64, ctx=None):
+    return ORIG_CONV(xp, w, bias, act, dtype)
+
+
+def _conv_context_reversed(xp, w, bias=None, act=None, dtype=np.float64, ctx=None):
+    return ORIG_CONV(xp, w, bias, act, dtype, ctx=None if ctx is None else np.asarray(ctx)[::-1])
 
 
 ORIG_CONV = oconv.conv_on_path
@@ -77,10 +85,25 @@ CONV_PINS = [
     lambda: pins.test_conv_chain_matches_torch_conv1d(None, 4),
     pins.test_conv_onehot_reads_path_history_bitwise,
     lambda: pins.test_conv_tree_matches_brute_force(None),
+    pins.test_conv_root_context_is_the_eq11_concatenation,
+    pins.test_conv_context_out_is_the_path_walk,
 ]
 
 
-@pytest.mark.parametrize("bad", [_conv_taps_reversed, _conv_no_padding_history])
+@pytest.mark.parametrize("bad", [_conv_taps_reversed, _conv_no_padding_history, _conv_context_ignored,
+                                 _conv_context_reversed])
 def test_planted_conv_mistake_is_caught(monkeypatch, bad):
     monkeypatch.setattr(oconv, "conv_on_path", bad)
     assert _fails(CONV_PINS)
+
+
+def _gdn_init_ignored(q, k, v, g, beta, scale=1.0, snap_at=(), heads=None, init=None, dtype=np.float64):
+    return ORIG_GDN(q, k, v, g, beta, scale, snap_at, heads, None, dtype)
+
+
+ORIG_GDN = ogdn.gdn_on_path
+
+
+def test_planted_initial_state_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(ogdn, "gdn_on_path", _gdn_init_ignored)
+    assert _fails([pins.test_partition_gateway_reproduces_the_uncut_trie])

@@ -16,6 +16,7 @@ from oracle import conv as oconv
 from oracle import gdn as ogdn
 from oracle import trie as otrie
 from oracle.brute import _prev_token_fn, conv_brute, gdn_brute
+from tests import parity
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -337,3 +338,82 @@ def test_oracle_on_tiny_workload_every_path():
     off = otrie.segment_offsets(wl.seg_lens)
     assert np.array_equal(op[-16:], o[off[3]:off[4]]) and np.array_equal(snaps[len(idx) - 1], st[3])
     assert round(otrie.por(wl.parents, wl.seg_lens), 4) == round(1 - 192 / 448, 4)
+
+
+# ------------------------------------------------------- partition gateways
+
+def test_conv_root_context_is_the_eq11_concatenation():
+    """Eq. 11, y = Conv([ctx; x])[W-1:]: a root's given context computed by
+    prepending it to the path and dropping the first W-1 outputs; in a
+    forest, root r reads context r (roots in segment order)."""
+    rng = np.random.default_rng(21)
+    for W in (2, 4):
+        x = rng.standard_normal((9, 5))
+        w = rng.standard_normal((5, W))
+        ctx = rng.standard_normal((W - 1, 5))
+        assert np.array_equal(oconv.conv_on_path(x, w, ctx=ctx),
+                              oconv.conv_on_path(np.concatenate([ctx, x]), w)[W - 1:])
+        parents, lens = np.array([-1, 0, -1, 2]), np.array([3, 2, 4, 1])
+        xs = rng.standard_normal((10, 5))
+        init = rng.standard_normal((2, W - 1, 5))
+        y = oconv.tree_conv_reference(parents, lens, xs, w, init_ctx=init)
+        assert np.array_equal(y[:5], oconv.conv_on_path(np.concatenate([init[0], xs[:5]]), w)[W - 1:])
+        assert np.array_equal(y[5:], oconv.conv_on_path(np.concatenate([init[1], xs[5:]]), w)[W - 1:])
+
+
+def test_conv_context_out_is_the_path_walk():
+    """The W-1 inputs ending at a segment's last token, by walking the path
+    token by token and, past the root, into its given context (newest
+    first)."""
+    rng = np.random.default_rng(22)
+    W, C = 4, 3
+    parents, lens = rand_trie(rng, 12, 3, n_roots=2)
+    n = int(lens.sum())
+    x = rng.standard_normal((n, C))
+    init = rng.standard_normal((2, W - 1, C))
+    got = oconv.conv_context_reference(parents, lens, x, W, init_ctx=init)
+    prev, _, start = _prev_token_fn(parents, lens)
+    roots = [s for s in range(len(parents)) if parents[s] < 0]
+    for s in range(len(parents)):
+        root = s
+        while parents[root] >= 0:
+            root = parents[root]
+        j, m = start[s] + int(lens[s]) - 1, 0
+        for back in range(W - 1):  # row W-2-back is `back` steps before the last token
+            if back > 0 and j is not None:
+                j = prev(j)
+            if j is None:
+                m += 1
+                want = init[roots.index(root)][W - 1 - m]
+            else:
+                want = x[j]
+            assert np.array_equal(got[s, W - 2 - back], want), (s, back)
+
+
+def test_partition_gateway_reproduces_the_uncut_trie():
+    """Section 3.3 / appendix B.7: cutting a subtree off into its own
+    partition, whose root starts from the parent's final state and conv
+    context, reproduces the uncut trie bitwise (conv and recurrence)."""
+    rng = np.random.default_rng(23)
+    W, C = 4, 4
+    parents, lens = rand_trie(rng, 14, 4, n_roots=1)
+    n = int(lens.sum())
+    off = otrie.segment_offsets(lens)
+    x = rng.standard_normal((n, C))
+    wts = rng.standard_normal((C, W))
+    q, k, v, g, beta = scan_inputs(rng, n, 1, 2, 3, 4)
+    yF = oconv.tree_conv_reference(parents, lens, x, wts)
+    oF, sF = ogdn.tree_gdn_reference(parents, lens, q, k, v, g, beta)
+    for c in [s for s in range(1, len(parents)) if parents[s] >= 0][:4]:
+        keep, pa, ia, subl, pb, ib = parity.split_subtree(parents, c)
+        rows = lambda segs: np.concatenate([np.arange(off[s], off[s + 1]) for s in segs])
+        ra, rb = rows(keep), rows(subl)
+        la, lb = lens[keep], lens[subl]
+        ctxA = oconv.conv_context_reference(pa, la, x[ra], W)
+        oA, sA = ogdn.tree_gdn_reference(pa, la, q[ra], k[ra], v[ra], g[ra], beta[ra])
+        par = ia[int(parents[c])]
+        yB = oconv.tree_conv_reference(pb, lb, x[rb], wts, init_ctx=ctxA[par][None])
+        oB, sB = ogdn.tree_gdn_reference(pb, lb, q[rb], k[rb], v[rb], g[rb], beta[rb], init_states=sA[par][None])
+        assert np.array_equal(yB, yF[rb]) and np.array_equal(oB, oF[rb])
+        assert np.array_equal(sB, sF[subl])
+        assert np.array_equal(oA, oF[ra]) and np.array_equal(sA, sF[keep])

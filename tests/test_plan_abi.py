@@ -69,17 +69,29 @@ def test_plan_por_printed_example():
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_conv_history_is_the_path_history(W, seed):
     """hist[s][W-2-j] must be the packed row j+1 steps before segment s's first
-    token along its path (walked token by token), -1 before the root."""
+    token along its path (walked token by token); m steps before the root
+    it is the code -1 - (r (W-1) + W-1-m) of row W-1-m of root r's context
+    (r = the root's rank among the roots in segment order)."""
     rng = np.random.default_rng(seed)
     parents, lens = rand_trie(rng, 50, 4, n_roots=3)
     plan = _lib.TreePlan(parents, lens, W)
     hist = plan.conv_history()
     prev, _, start = _prev_token_fn(parents, lens)
+    rank = {r: i for i, r in enumerate(s for s in range(len(parents)) if parents[s] < 0)}
     for s in range(len(parents)):
-        j = start[s]
+        root = s
+        while parents[root] >= 0:
+            root = parents[root]
+        j, m = start[s], 0
         for back in range(1, W):
-            j = None if j is None else prev(j)
-            assert hist[s, W - 1 - back] == (-1 if j is None else j), (s, back)
+            if j is not None:
+                j = prev(j)
+            if j is None:
+                m += 1
+                want = -1 - (rank[root] * (W - 1) + (W - 1 - m))
+            else:
+                want = j
+            assert hist[s, W - 1 - back] == want, (s, back)
 
 
 def test_levels_respect_depth_and_longest_first():
@@ -121,13 +133,16 @@ def test_argument_errors_need_no_device():
     plan = _lib.TreePlan(p, n, 4)
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     # token count mismatch
-    assert lib.tree_conv(fake, fake, None, fake, 6, 8, 1, 0, plan.handle, fake, None) == -3
+    assert lib.tree_conv(fake, fake, None, fake, None, None, 6, 8, 1, 0, plan.handle, fake, None) == -3
     # bad activation / dtype
-    assert lib.tree_conv(fake, fake, None, fake, 5, 8, 1, 7, plan.handle, fake, None) == -1
-    assert lib.tree_conv(fake, fake, None, fake, 5, 8, 5, 0, plan.handle, fake, None) == -1
-    assert lib.tree_conv(fake, fake, None, fake, 5, 8, 1, 0, plan.handle, None, None) == -1
+    assert lib.tree_conv(fake, fake, None, fake, None, None, 5, 8, 1, 7, plan.handle, fake, None) == -1
+    assert lib.tree_conv(fake, fake, None, fake, None, None, 5, 8, 5, 0, plan.handle, fake, None) == -1
+    assert lib.tree_conv(fake, fake, None, fake, None, None, 5, 8, 1, 0, plan.handle, None, None) == -1
+    # context out aliasing an input
+    assert lib.tree_conv(fake, fake, None, ctypes.c_void_p(0x2000), None, fake, 5, 8, 1, 0, plan.handle,
+                         fake, None) == -1
     scan = lib.tree_gdn_scan
-    args = [fake] * 7
+    args = [fake] * 6 + [None, fake]  # q, k, v, g, beta, o, init_states, states
     assert scan(*args, 5, 2, 3, 128, 128, 1.0, 1, 0, plan.handle, fake, fake, 1 << 30, None) == -4
     assert scan(*args, 5, 1, 1, 64, 64, 1.0, 1, 0, plan.handle, fake, fake, 1 << 30, None) == -4
     assert scan(*args, 5, 1, 1, 128, 128, 1.0, 0, 0, plan.handle, fake, fake, 1 << 30, None) == -4
@@ -145,7 +160,7 @@ def test_workspace_size_and_check():
     assert lib.tree_scan_workspace_bytes(plan.handle, 16, 128, 128, 1) == 0
     fake = ctypes.c_void_p(0x1000)
     n = plan.n_tokens
-    rc = lib.tree_gdn_scan(*([fake] * 6), None, n, 16, 16, 128, 128, 1.0, 1, 0, plan.handle, fake,
+    rc = lib.tree_gdn_scan(*([fake] * 6), None, None, n, 16, 16, 128, 128, 1.0, 1, 0, plan.handle, fake,
                            fake, need - 1, None)
     assert rc == -5
 
