@@ -3,8 +3,10 @@
     python bench.py [--steps K] [--warmup W] [--config 5] [--no-cpu-baseline]
 
 One step is one pass of the whole hot path over the resident synthetic batch:
-tree_conv over x [N, C] and tree_gdn_scan (one launch per trie level) over
-q, k, v, g, beta.  Inputs are generated on the GPU before timing; W untimed
+tree_conv over x [N, C] and tree_gdn_scan over q, k, v, g, beta under the
+fork/rescan policy (--schedule auto; the RL batch trie forks: one launch per
+trie level).  After the timed steps the other schedule is timed on the same
+trie (fork_vs_rescan in the output).  Inputs are generated on the GPU before timing; W untimed
 steps, then K timed steps between two synchronisations.  Kernel times come
 from HIP events recorded on the stream the kernels are launched on.
 
@@ -114,6 +116,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--schedule", choices=["auto", "level", "rescan"], default="auto",
+                    help="scan schedule of the timed step (auto = the fork/rescan policy)")
+    ap.add_argument("--no-rescan-compare", action="store_true",
+                    help="skip the untimed-by-the-step comparison run of the rescan schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="before timing, run one plain 1 GiB device copy (a counter reference for profiles)")
@@ -139,6 +145,7 @@ def main():
     ws_bytes = int(lib.tree_scan_workspace_bytes(plan.handle, s.h_v, s.d_k, s.d_v, 0))
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     plan.on_device(dev)
+    sched = plan.choose_schedule() if args.schedule == "auto" else args.schedule
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         torch.empty_like(src).copy_(src)
@@ -151,7 +158,8 @@ def main():
         ptp.tree_conv(t["x"], t["w"], plan, out=y)
         if ev:
             ev[1].record()
-        ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, out=o, workspace=ws)
+        ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, out=o, workspace=ws,
+                          schedule=sched)
         if ev:
             ev[2].record()
 
@@ -169,11 +177,29 @@ def main():
     scan_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     ms_per_step = 1e3 * wall / args.steps
 
+    # After the timed steps: the other schedule on the same trie, so the
+    # work a fork saves shows up as measured scan time.
+    other = None
+    if not args.no_rescan_compare:
+        alt = "rescan" if sched == "level" else "level"
+        reps = max(3, min(args.steps, 10))
+        for _ in range(2):
+            ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, out=o, workspace=ws,
+                              schedule=alt)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, out=o, workspace=ws,
+                              schedule=alt)
+        ev[1].record()
+        torch.cuda.synchronize()
+        other = {"schedule": alt, "scan_ms": ev[0].elapsed_time(ev[1]) / reps, "reps": reps}
+
     n = wl.n_tokens
     state_bytes = 2 * st["n_parents"] * s.h_v * s.d_k * s.d_v * 4  # write + read once
     conv_b = n * conv_bytes_per_token(s)
-    scan_b = n * scan_bytes_per_token(s) + state_bytes
-    n_levels = st["n_levels"]
+    scan_b = n * scan_bytes_per_token(s) + (state_bytes if sched == "level" else 0)
+    n_levels = st["n_levels"] if sched == "level" else 1
     kernels = {
         "tree_conv": {"ms": conv_ms, "bytes": conv_b, "launches": 1,
                       "GB/s": conv_b / conv_ms / 1e6},
@@ -205,6 +231,7 @@ def main():
             "path_tokens": st["path_tokens"],
             "work_saved_vs_rescan": st["path_tokens"] / n,
             "por": st["por"],
+            "scan_schedule": sched,
             "parallelism": "1 GPU",
         },
         "roofline": {
@@ -219,6 +246,13 @@ def main():
         "kernels": kernels,
         "roofline_combined_frac": ((conv_b + scan_b) / (HBM_PEAK_GBS * 1e9)) / ((conv_ms + scan_ms) * 1e-3),
     }
+    if other is not None:
+        fork_ms = scan_ms if sched == "level" else other["scan_ms"]
+        rescan_ms = other["scan_ms"] if sched == "level" else scan_ms
+        out["fork_vs_rescan"] = {"fork_scan_ms": fork_ms, "rescan_scan_ms": rescan_ms,
+                                 "measured_speedup": rescan_ms / fork_ms,
+                                 "path_tokens_over_n": st["path_tokens"] / n,
+                                 "rescan_reps": other["reps"]}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

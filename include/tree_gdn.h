@@ -62,7 +62,30 @@ extern "C" {
 #define TREE_ACT_NONE 0
 #define TREE_ACT_SILU 1
 
-#define TREE_SCHED_LEVEL 0 /* one launch per trie level; stream order is the barrier */
+/* Scan schedules (tree-recurrence 0.1.0 project page, "How a tree runs": a
+ * tree scan either forks or rescans).  Both give bitwise the same outputs and
+ * states: the chunks are segment-local either way and the state handed from
+ * a segment to its child is the same fp32 value. */
+#define TREE_SCHED_LEVEL 0  /* fork: one launch per trie level, each segment
+                               starting from its parent's final state; stream
+                               order is the barrier between levels            */
+#define TREE_SCHED_RESCAN 1 /* rescan: one launch over every root-to-leaf
+                               path, the state carried from segment to
+                               segment in registers; shared prefixes are
+                               scanned once per path through them and each
+                               segment's outputs and state are written by one
+                               of those paths                                 */
+#define TREE_SCHED_AUTO 2   /* tree_plan_choose_schedule with
+                               TREE_FORK_MIN_SAVED_TOKENS                     */
+
+/* Default price, in scanned tokens, of one extra launch (one more trie level)
+ * in the fork/rescan choice.  On MI355X a level launch is stream-ordered with
+ * no host round trip and costs about the scan of a hundred or so tokens;
+ * measured over RL-batch-shaped tries (1..64 prompts of 16..4096 tokens with
+ * 8 completions each, 16/32 heads of 128), thresholds from 113 to 448 lose
+ * the least time against the faster schedule
+ * (python -m prefix_tree_packed_plan_amd.calibrate_policy re-measures it). */
+#define TREE_FORK_MIN_SAVED_TOKENS 256
 
 typedef struct tree_plan tree_plan_t; /* opaque, host memory, immutable once built */
 
@@ -78,6 +101,9 @@ typedef struct tree_plan_stats {
   int32_t n_parents; /* segments with at least one child (they own a state slot) */
   int32_t n_levels;  /* 1 + the largest depth                                    */
   int32_t conv_width;
+  int64_t path_entries; /* rescan walk table size: sum over leaves of (depth + 1),
+                           or -1 when it is too large to build (2^26 entries)
+                           and TREE_SCHED_RESCAN is unavailable               */
 } tree_plan_stats_t;
 
 /*
@@ -116,6 +142,33 @@ int tree_plan_conv_history(const tree_plan_t* plan, int32_t* hist);
  * order[0..n_seg-1] (segments of level L are order[level_start[L] ..
  * level_start[L+1]-1], longest first, ties by index). */
 int tree_plan_levels(const tree_plan_t* plan, int32_t* level_start, int32_t* order);
+
+/*
+ * tree_plan_paths -- copy the rescan walk table: path_off[0..n_leaves]
+ * (int32) and path_seg[0..path_entries-1].  Walk w covers path_seg[path_off[w]
+ * .. path_off[w+1]-1], the segments of one leaf's root path from the root
+ * down; walks are ordered by path length, longest first (ties by leaf
+ * index).  An entry is the segment index s when this walk writes s's outputs
+ * and state (the walk of the lowest-indexed leaf below s), ~s otherwise, so
+ * every segment is written by exactly one walk.
+ * Errors: INVALID_ARG, UNSUPPORTED (table not built: path_entries == -1).
+ */
+int tree_plan_paths(const tree_plan_t* plan, int32_t* path_off, int32_t* path_seg);
+
+/*
+ * tree_plan_choose_schedule -- the fork/rescan policy (tree-recurrence 0.1.0
+ * project page, "How a tree runs": fork when the prefix tokens it saves
+ * outweigh one more kernel call per level).  With saved = path_tokens -
+ * n_tokens (tokens a rescan would scan twice or more) and n_levels - 1 extra
+ * launches for the fork, *sched = TREE_SCHED_LEVEL when
+ *     saved >= fork_min_saved_tokens * (n_levels - 1)
+ * (always for a single-level trie, where both are one launch), else
+ * TREE_SCHED_RESCAN; LEVEL whenever the walk table is unavailable.
+ * fork_min_saved_tokens >= 0 is the price of one launch in scanned tokens
+ * (TREE_FORK_MIN_SAVED_TOKENS by default).
+ * Errors: INVALID_ARG.
+ */
+int tree_plan_choose_schedule(const tree_plan_t* plan, int64_t fork_min_saved_tokens, int32_t* sched);
 
 /* Bytes of device memory tree_plan_upload writes (the device copy of the plan). */
 size_t tree_plan_device_bytes(const tree_plan_t* plan);
@@ -164,9 +217,10 @@ int tree_conv(const void* x, const void* w, const void* bias, void* y, const voi
               const tree_plan_t* plan, const void* dplan, void* stream);
 
 /*
- * tree_scan_workspace_bytes -- device workspace tree_gdn_scan needs: one fp32
- * state [h_v, d_k, d_v] per segment with children (0 when the caller passes
- * `states`, which then carries the parent states).
+ * tree_scan_workspace_bytes -- device workspace tree_gdn_scan needs under
+ * TREE_SCHED_LEVEL (or AUTO): one fp32 state [h_v, d_k, d_v] per segment with
+ * children (0 when the caller passes `states`, which then carries the parent
+ * states).  TREE_SCHED_RESCAN needs none.
  */
 size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d_k, int32_t d_v,
                                  int32_t with_states);
@@ -193,10 +247,13 @@ size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d
  * dtype  TREE_DTYPE_BF16 (bf16 MFMA, fp32 accumulation, compensated
  *        split-bf16 on the state path) or TREE_DTYPE_F32 (inputs split into
  *        two bf16 parts on every product).
- * sched  TREE_SCHED_LEVEL.
- * ws     device workspace of ws_bytes >= tree_scan_workspace_bytes.
+ * sched  TREE_SCHED_LEVEL, TREE_SCHED_RESCAN or TREE_SCHED_AUTO (see
+ *        tree_plan_choose_schedule).
+ * ws     device workspace of ws_bytes >= tree_scan_workspace_bytes (may be
+ *        NULL under TREE_SCHED_RESCAN).
  * Compiled head sizes: d_k = d_v in {32, 128} for bf16, 32 for fp32.
- * Errors: INVALID_ARG, SIZE, UNSUPPORTED, WORKSPACE, HIP.
+ * Errors: INVALID_ARG, SIZE, UNSUPPORTED (also: RESCAN without a walk
+ * table), WORKSPACE, HIP.
  */
 int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, void* o, const float* init_states, float* states,

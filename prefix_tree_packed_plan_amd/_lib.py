@@ -27,7 +27,9 @@ ERRORS = {
 }
 DTYPE_F32, DTYPE_BF16 = 0, 1
 ACT_NONE, ACT_SILU = 0, 1
-SCHED_LEVEL = 0
+SCHED_LEVEL, SCHED_RESCAN, SCHED_AUTO = 0, 1, 2
+SCHEDULES = {"level": SCHED_LEVEL, "rescan": SCHED_RESCAN, "auto": SCHED_AUTO}
+FORK_MIN_SAVED_TOKENS = 256  # the header's default price of one extra launch
 
 # Every function the header declares, with its ctypes signature.
 _P, _I32, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -45,6 +47,7 @@ class PlanStats(ctypes.Structure):
         ("n_parents", ctypes.c_int32),
         ("n_levels", ctypes.c_int32),
         ("conv_width", ctypes.c_int32),
+        ("path_entries", ctypes.c_int64),
     ]
 
 
@@ -54,6 +57,8 @@ SIGNATURES = {
     "tree_plan_query": (ctypes.c_int, [_P, ctypes.POINTER(PlanStats)]),
     "tree_plan_conv_history": (ctypes.c_int, [_P, _P]),
     "tree_plan_levels": (ctypes.c_int, [_P, _P, _P]),
+    "tree_plan_paths": (ctypes.c_int, [_P, _P, _P]),
+    "tree_plan_choose_schedule": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_I32)]),
     "tree_plan_device_bytes": (_SZ, [_P]),
     "tree_plan_upload": (ctypes.c_int, [_P, _P, _SZ, _P]),
     "tree_conv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]),
@@ -151,6 +156,23 @@ class TreePlan:
         _check(load().tree_plan_levels(self._h, ls.ctypes.data, order.ctypes.data))
         return ls, order
 
+    def paths(self):
+        """Rescan walks: (path_off [n_leaves + 1], path_seg [path_entries]);
+        an entry is a segment the walk writes, or ~segment if another walk
+        writes it."""
+        n = int(self.stats["path_entries"])
+        off = np.zeros(self.stats["n_leaves"] + 1, np.int32)
+        seg = np.zeros(max(n, 1), np.int32)
+        _check(load().tree_plan_paths(self._h, off.ctypes.data, seg.ctypes.data))
+        return off, seg[:n]
+
+    def choose_schedule(self, fork_min_saved_tokens: int = FORK_MIN_SAVED_TOKENS) -> str:
+        """The fork/rescan policy: "level" when the prefix tokens forking saves
+        reach fork_min_saved_tokens per extra launch, else "rescan"."""
+        out = _I32()
+        _check(load().tree_plan_choose_schedule(self._h, int(fork_min_saved_tokens), ctypes.byref(out)))
+        return {SCHED_LEVEL: "level", SCHED_RESCAN: "rescan"}[out.value]
+
     def device_bytes(self) -> int:
         return int(load().tree_plan_device_bytes(self._h))
 
@@ -243,11 +265,13 @@ def tree_conv(x, w, plan: TreePlan, bias=None, act: Optional[str] = None, out=No
 
 
 def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_states: bool = False,
-                  out=None, states=None, workspace=None, init_states=None):
+                  out=None, states=None, workspace=None, init_states=None, schedule: str = "auto",
+                  fork_min_saved_tokens: int = FORK_MIN_SAVED_TOKENS):
     """Tree gated delta rule: o [N, H_v, d_v] (and states [n_seg, H_v, d_k, d_v] fp32).
 
     init_states [n_roots, H_v, d_k, d_v] fp32: the states the roots start
-    from (default zero)."""
+    from (default zero).  schedule: "level" (fork), "rescan" or "auto"
+    (plan.choose_schedule(fork_min_saved_tokens)); all give the same bits."""
     import torch
     _need(q, "q")
     dev = q.device
@@ -271,8 +295,15 @@ def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_s
         _need(init_states, "init_states", torch.float32, dev)
         if tuple(init_states.shape) != (plan.n_roots, h_v, d_k, d_v):
             raise ValueError("init_states must be [n_roots, H_v, d_k, d_v]")
+    if schedule not in SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}")
+    if schedule == "auto":
+        schedule = plan.choose_schedule(fork_min_saved_tokens)
+    sched = SCHEDULES[schedule]
     lib = load()
-    need = int(lib.tree_scan_workspace_bytes(plan.handle, h_v, d_k, d_v, int(states is not None)))
+    need = 0
+    if sched == SCHED_LEVEL:
+        need = int(lib.tree_scan_workspace_bytes(plan.handle, h_v, d_k, d_v, int(states is not None)))
     if need > 0 and (workspace is None or workspace.numel() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     dplan = plan.on_device(dev)
@@ -280,7 +311,7 @@ def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_s
     _check(lib.tree_gdn_scan(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                              o.data_ptr(), init_states.data_ptr() if init_states is not None else None,
                              states.data_ptr() if states is not None else None,
-                             n, h_qk, h_v, d_k, d_v, float(scale), _dtype_code(q), SCHED_LEVEL,
+                             n, h_qk, h_v, d_k, d_v, float(scale), _dtype_code(q), sched,
                              plan.handle, dplan.data_ptr(),
                              workspace.data_ptr() if workspace is not None else None,
                              workspace.numel() if workspace is not None else 0, stream))

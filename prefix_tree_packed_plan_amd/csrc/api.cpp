@@ -71,6 +71,26 @@ int tree_plan_query(const tree_plan_t* plan, tree_plan_stats_t* out) {
   out->n_parents = p.n_parents;
   out->n_levels = p.n_levels;
   out->conv_width = p.width;
+  out->path_entries = p.paths_ok ? p.path_entries : -1;
+  return TREE_OK;
+}
+
+int tree_plan_paths(const tree_plan_t* plan, int32_t* path_off, int32_t* path_seg) {
+  if (!plan || !path_off || !path_seg) return fail(TREE_ERR_INVALID_ARG, "tree_plan_paths: null argument");
+  if (!plan->p.paths_ok)
+    return fail(TREE_ERR_UNSUPPORTED, "tree_plan_paths: walk table of %lld entries not built",
+                static_cast<long long>(plan->p.path_entries));
+  std::copy(plan->p.path_off.begin(), plan->p.path_off.end(), path_off);
+  std::copy(plan->p.path_seg.begin(), plan->p.path_seg.end(), path_seg);
+  return TREE_OK;
+}
+
+int tree_plan_choose_schedule(const tree_plan_t* plan, int64_t fork_min_saved_tokens, int32_t* sched) {
+  if (!plan || !sched) return fail(TREE_ERR_INVALID_ARG, "tree_plan_choose_schedule: null argument");
+  if (fork_min_saved_tokens < 0)
+    return fail(TREE_ERR_INVALID_ARG, "tree_plan_choose_schedule: fork_min_saved_tokens %lld < 0",
+                static_cast<long long>(fork_min_saved_tokens));
+  *sched = tg::choose_schedule(plan->p, fork_min_saved_tokens);
   return TREE_OK;
 }
 
@@ -146,11 +166,17 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, c
   if (h_v % h_qk != 0)
     return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan: h_v %d is not a multiple of h_qk %d", h_v, h_qk);
   if (!dtype_ok(dtype)) return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: bad dtype %d", dtype);
-  if (sched != TREE_SCHED_LEVEL) return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: bad schedule %d", sched);
+  if (sched == TREE_SCHED_AUTO) sched = tg::choose_schedule(p, TREE_FORK_MIN_SAVED_TOKENS);
+  if (sched != TREE_SCHED_LEVEL && sched != TREE_SCHED_RESCAN)
+    return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: bad schedule %d", sched);
+  if (sched == TREE_SCHED_RESCAN && !p.paths_ok)
+    return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan: rescan walk table of %lld entries not built",
+                static_cast<long long>(p.path_entries));
   if (!tg::scan_supported(d_k, d_v, dtype))
     return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan: d_k=%d d_v=%d dtype=%d not compiled in", d_k,
                 d_v, dtype);
-  const size_t need = tree_scan_workspace_bytes(plan, h_v, d_k, d_v, states != nullptr);
+  const size_t need =
+      sched == TREE_SCHED_LEVEL ? tree_scan_workspace_bytes(plan, h_v, d_k, d_v, states != nullptr) : 0;
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(TREE_ERR_WORKSPACE, "tree_gdn_scan: workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0,
                 need);
@@ -173,10 +199,18 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, c
   a.h_v = h_v;
   a.scale = scale;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (sched == TREE_SCHED_RESCAN) {
+    a.walk_off = base + p.m_path_off;
+    a.walk = base + p.m_path_seg;
+    a.n_items = p.n_leaves;
+    const hipError_t e = tg::launch_scan(a, d_k, d_v, dtype, true, st);
+    if (e != hipSuccess) return hip_fail("tree_gdn_scan: launch", e);
+    return TREE_OK;
+  }
   for (int32_t l = 0; l < p.n_levels; ++l) {
     a.items = base + p.m_order + p.level_start[l];
     a.n_items = p.level_start[l + 1] - p.level_start[l];
-    const hipError_t e = tg::launch_scan_level(a, d_k, d_v, dtype, st);
+    const hipError_t e = tg::launch_scan(a, d_k, d_v, dtype, false, st);
     if (e != hipSuccess) return hip_fail("tree_gdn_scan: launch", e);
   }
   return TREE_OK;

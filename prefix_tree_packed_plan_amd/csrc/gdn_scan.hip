@@ -160,7 +160,12 @@ struct Smem {
   alignas(16) float bet[G][CH];
 };
 
-template <int DK, int DV, bool F32IN, int G>
+// PATHS = false: block item = one segment of a level, starting from its
+// parent's state.  PATHS = true: block item = one rescan walk, the segments
+// of a root-to-leaf path in order with the state carried in registers from
+// one to the next; outputs and states are written only for the segments the
+// walk owns.
+template <int DK, int DV, bool F32IN, int G, bool PATHS>
 __global__ __launch_bounds__(64 * G * (DV / 32)) void gdn_level_kernel(ScanArgs args) {
   constexpr int NWV = DV / 32;  // waves per value head
   constexpr int NW = G * NWV;
@@ -186,9 +191,18 @@ __global__ __launch_bounds__(64 * G * (DV / 32)) void gdn_level_kernel(ScanArgs 
   const int grp = blockIdx.x - item * n_grp;
   const int h = grp * G + vh;
   const int hq = (grp * G) / (args.h_v / args.h_qk);
-  const int seg = args.items[item];
-  const int seg_beg = args.seg_off[seg];
-  const int seg_end = args.seg_off[seg + 1];
+  int wj = 0, wend = 0;  // walk cursor (PATHS)
+  int seg;
+  bool own = true;  // this block writes the current segment's outputs and state
+  if (PATHS) {
+    wj = args.walk_off[item];
+    wend = args.walk_off[item + 1];
+    const int e = args.walk[wj];
+    seg = e < 0 ? ~e : e;
+    own = e >= 0;
+  } else {
+    seg = args.items[item];
+  }
   const int par = args.parent[seg];
 
   // ---- initial state (parent's final state, or zero) ------------------------
@@ -248,6 +262,9 @@ __global__ __launch_bounds__(64 * G * (DV / 32)) void gdn_level_kernel(ScanArgs 
   TIn* ost = reinterpret_cast<TIn*>(&sm.qk[0][0][0]) + w * CH * 32;
   static_assert(sizeof(TIn) * NW * CH * 32 <= sizeof(sm.qk), "output staging fits");
 
+  for (;;) {
+  const int seg_beg = args.seg_off[seg];
+  const int seg_end = args.seg_off[seg + 1];
   for (int t0 = seg_beg; t0 < seg_end; t0 += CH) {
     const int Lc = min(CH, seg_end - t0);
 
@@ -567,7 +584,7 @@ __global__ __launch_bounds__(64 * G * (DV / 32)) void gdn_level_kernel(ScanArgs 
       const int row = ci / CPR, c = ci % CPR;
       const int col = (EPO * c) ^ (EPO * ((row >> 2) & 3));
       const uint4 val = *reinterpret_cast<const uint4*>(&ost[row * 32 + col]);
-      if (row < Lc)
+      if (own && row < Lc)
         *reinterpret_cast<uint4*>(og + (static_cast<size_t>(t0 + row) * args.h_v + h) * DV + 32 * cw + EPO * c) = val;
     }
 
@@ -575,10 +592,13 @@ __global__ __launch_bounds__(64 * G * (DV / 32)) void gdn_level_kernel(ScanArgs 
 
   // ---- segment end: publish the state for the children / the caller --------
   float* dst = nullptr;
-  if (args.states)
+  if (PATHS) {
+    if (own) dst = args.states ? args.states + (static_cast<size_t>(seg) * args.h_v + h) * head_elems : nullptr;
+  } else if (args.states) {
     dst = args.states + (static_cast<size_t>(seg) * args.h_v + h) * head_elems;
-  else if (args.slot[seg] >= 0)
+  } else if (args.slot[seg] >= 0) {
     dst = args.slots + (static_cast<size_t>(args.slot[seg]) * args.h_v + h) * head_elems;
+  }
   if (dst) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -587,12 +607,20 @@ __global__ __launch_bounds__(64 * G * (DV / 32)) void gdn_level_kernel(ScanArgs 
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[(16 * mt + 4 * h4 + r) * DV + 32 * cw + 16 * nt + i16] = S[mt][nt][r];
   }
+  if (!PATHS || ++wj == wend) break;
+  const int e = args.walk[wj];  // the next segment of the walk
+  seg = e < 0 ? ~e : e;
+  own = e >= 0;
+  }
 }
 
 template <int DK, int DV, bool F32IN, int G>
-hipError_t launch_one(const ScanArgs& a, hipStream_t stream) {
+hipError_t launch_one(const ScanArgs& a, bool paths, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.n_items) * (a.h_v / G));
-  gdn_level_kernel<DK, DV, F32IN, G><<<grid, 64 * G * (DV / 32), 0, stream>>>(a);
+  if (paths)
+    gdn_level_kernel<DK, DV, F32IN, G, true><<<grid, 64 * G * (DV / 32), 0, stream>>>(a);
+  else
+    gdn_level_kernel<DK, DV, F32IN, G, false><<<grid, 64 * G * (DV / 32), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -604,11 +632,11 @@ bool scan_supported(int d_k, int d_v, int dtype) {
   return d_k == 32 || d_k == 128;
 }
 
-hipError_t launch_scan_level(const ScanArgs& a, int d_k, int d_v, int dtype, hipStream_t stream) {
+hipError_t launch_scan(const ScanArgs& a, int d_k, int d_v, int dtype, bool paths, hipStream_t stream) {
   const bool f32 = dtype == TREE_DTYPE_F32;
-  if (d_k == 128 && d_v == 128 && !f32) return launch_scan_d128(a, stream);
+  if (d_k == 128 && d_v == 128 && !f32) return launch_scan_d128(a, paths, stream);
   if (d_k == 32 && d_v == 32)
-    return f32 ? launch_one<32, 32, true, 1>(a, stream) : launch_one<32, 32, false, 1>(a, stream);
+    return f32 ? launch_one<32, 32, true, 1>(a, paths, stream) : launch_one<32, 32, false, 1>(a, paths, stream);
   return hipErrorInvalidValue;
 }
 

@@ -196,6 +196,12 @@ __device__ __forceinline__ f32x4 gram(const char* X, const char* Y, const int* a
   return acc;
 }
 
+// PATHS = false: block item = one segment of a level, starting from its
+// parent's state.  PATHS = true: block item = one rescan walk, the segments
+// of a root-to-leaf path in order with the state carried in registers from
+// one to the next; outputs and states are written only for the segments the
+// walk owns.
+template <bool PATHS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4))) void gdn_d128_kernel(ScanArgs args) {
   __shared__ Smem sm;
 
@@ -222,9 +228,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
   }
   const int hq = h / (args.h_v / args.h_qk);
-  const int seg = args.items[item];
+  int wj = 0, wend = 0;  // walk cursor (PATHS)
+  int seg;
+  bool own = true;  // this block writes the current segment's outputs and state
+  if (PATHS) {
+    wj = args.walk_off[item];
+    wend = args.walk_off[item + 1];
+    const int e = args.walk[wj];
+    seg = e < 0 ? ~e : e;
+    own = e >= 0;
+  } else {
+    seg = args.items[item];
+  }
   const int seg_beg = args.seg_off[seg];
-  const int seg_end = args.seg_off[seg + 1];
+  int seg_end = args.seg_off[seg + 1];
   const int par = args.parent[seg];
   const uint16_t* qg = static_cast<const uint16_t*>(args.q);
   const uint16_t* kg = static_cast<const uint16_t*>(args.k);
@@ -269,13 +286,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   // Chunk at token tc into buffer buf: wave cw loads block cw (rows
   // 4cw..4cw+3) of the K, Q and V tiles; waves 4 and 5 the gate rows.  In a
   // partial chunk, rows past the end repeat row Ln - 1.
-  auto fetch = [&](int tc, int buf) {
+  auto fetch = [&](int tc, int end, int buf) {
     // Offsets of once-per-chunk accesses are recomputed from an opaque copy
     // of the lane number rather than held in registers across the loop.
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int cofs = 16 * ((ln & 15) ^ (4 * (ln >> 4)));  // this lane's 16-byte chunk of a row
-    const int Ln = min(CH, seg_end - tc);
+    const int Ln = min(CH, end - tc);
     const auto rk = rsrc(kg + (static_cast<size_t>(tc) * args.h_qk + hq) * D, CH * rs_qk);
     const auto rq = rsrc(qg + (static_cast<size_t>(tc) * args.h_qk + hq) * D, CH * rs_qk);
     const auto rv = rsrc(vg + (static_cast<size_t>(tc) * args.h_v + h) * D, CH * rs_v);
@@ -305,19 +322,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     __builtin_amdgcn_raw_buffer_store_b128(v, ro, orow * rs_v + 16 * (ln & 15), 0, 0);
   };
 
-  fetch(seg_beg, 0);
+  fetch(seg_beg, seg_end, 0);
   int s = 0;
   int prev_t0 = -1, prev_L = 0;
+  bool prev_own = true;
 
-  for (int t0 = seg_beg; t0 < seg_end; t0 += CH, s ^= 1) {
+  for (int t0 = seg_beg;;) {
     const int Lc = min(CH, seg_end - t0);
     const char* Ks = sm.kb[s];
     const char* Qs = sm.qb[s];
     const char* Vs = sm.vb[s];
+    // Next chunk: the rest of this segment, else (walks) the start of the
+    // next segment on the path.
+    int nt0 = t0 + CH, nend = seg_end, nseg = seg;
+    if (PATHS && nt0 >= seg_end && wj + 1 < wend) {
+      const int e = args.walk[wj + 1];
+      nseg = e < 0 ? ~e : e;
+      nt0 = args.seg_off[nseg];
+      nend = args.seg_off[nseg + 1];
+    }
+    const bool more = nt0 < nend;
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of the chunk has landed
     __syncthreads();                                   // (A) ... and every other wave's
-    if (t0 + CH < seg_end) fetch(t0 + CH, s ^ 1);
+    if (more) fetch(nt0, nend, s ^ 1);
 
     // -- gates, per wave: inclusive prefix of g over rows of 16 lanes (DPP),
     //    then row 1 adds row 0's total
@@ -458,7 +486,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
     // The previous chunk's output rows leave here, after the next chunk's
     // DMA has been issued, so they do not queue ahead of it.
-    if (prev_t0 >= 0) store_out(prev_t0, prev_L);
+    if (prev_t0 >= 0 && prev_own) store_out(prev_t0, prev_L);
     __syncthreads();  // (D) the inverse, -A and P^T operands of every wave are in LDS
 
     // -- state, part 2: block solve, output and state update
@@ -503,28 +531,55 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
     prev_t0 = t0;
     prev_L = Lc;
+    prev_own = own;
+    if (PATHS && t0 + CH >= seg_end) {  // a walk's segment ends: its owner publishes the state
+      if (own && args.states) {
+        // Lane offsets from an opaque copy of the lane number, so that no
+        // address of this once-per-segment store is held across the loop.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        float* dst = args.states + (static_cast<size_t>(seg) * args.h_v + h) * head_elems +
+                     (4 * (ln >> 4)) * D + col_w + (ln & 15);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(16 * mt + r) * D] = S[mt][r];
+      }
+      if (more) own = args.walk[++wj] >= 0;
+    }
+    if (!more) break;
+    t0 = nt0;
+    seg_end = nend;
+    seg = nseg;
+    s ^= 1;
   }
   __syncthreads();  // every wave's staged rows of the last chunk
-  store_out(prev_t0, prev_L);
+  if (prev_own) store_out(prev_t0, prev_L);
 
   // ---- segment end: publish the state -------------------------------------------
-  float* dst = nullptr;
-  if (args.states)
-    dst = args.states + (static_cast<size_t>(seg) * args.h_v + h) * head_elems;
-  else if (args.slot[seg] >= 0)
-    dst = args.slots + (static_cast<size_t>(args.slot[seg]) * args.h_v + h) * head_elems;
-  if (dst) {
+  if (!PATHS) {
+    float* dst = nullptr;
+    if (args.states)
+      dst = args.states + (static_cast<size_t>(seg) * args.h_v + h) * head_elems;
+    else if (args.slot[seg] >= 0)
+      dst = args.slots + (static_cast<size_t>(args.slot[seg]) * args.h_v + h) * head_elems;
+    if (dst) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * mt + 4 * h4 + r) * D + col_w + i16] = S[mt][r];
+        for (int r = 0; r < 4; ++r) dst[(16 * mt + 4 * h4 + r) * D + col_w + i16] = S[mt][r];
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_scan_d128(const ScanArgs& a, hipStream_t stream) {
-  gdn_d128_kernel<<<dim3(static_cast<unsigned>(a.n_items) * a.h_v), 64 * NW, 0, stream>>>(a);
+hipError_t launch_scan_d128(const ScanArgs& a, bool paths, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(a.n_items) * a.h_v);
+  if (paths)
+    gdn_d128_kernel<true><<<grid, 64 * NW, 0, stream>>>(a);
+  else
+    gdn_d128_kernel<false><<<grid, 64 * NW, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -42,19 +42,22 @@ struct ScanArgs {
   const int32_t* seg_off;
   const int32_t* parent;
   const int32_t* slot;
-  const int32_t* items;  // segments of this launch
-  int32_t n_items;
+  const int32_t* items;     // segments of this launch (level mode)
+  const int32_t* walk_off;  // rescan walks: walk w is walk[walk_off[w] .. walk_off[w+1]-1]
+  const int32_t* walk;      // segment index (owned) or its complement (not owned)
+  int32_t n_items;          // segments (level mode) or walks (rescan mode)
   int32_t h_qk;
   int32_t h_v;
   float scale;
 };
 
-// One launch over `n_items` segments x h_v value heads.  Returns
+// One launch over `n_items` work items x h_v value heads: segments of one
+// level (paths = false) or rescan walks (paths = true).  Returns
 // hipErrorInvalidValue for a head size that is not compiled in.
-hipError_t launch_scan_level(const ScanArgs& a, int d_k, int d_v, int dtype, hipStream_t stream);
+hipError_t launch_scan(const ScanArgs& a, int d_k, int d_v, int dtype, bool paths, hipStream_t stream);
 
 // bf16, d_k = d_v = 128: the DMA-fed kernel (gdn_scan_d128.hip).
-hipError_t launch_scan_d128(const ScanArgs& a, hipStream_t stream);
+hipError_t launch_scan_d128(const ScanArgs& a, bool paths, hipStream_t stream);
 
 // Whether (d_k, d_v, dtype) has a compiled scan kernel.
 bool scan_supported(int d_k, int d_v, int dtype);

@@ -16,6 +16,16 @@ std::string fmt(const char* f, long a, long b = 0, long c = 0) {
 }
 }  // namespace
 
+int32_t choose_schedule(const Plan& p, int64_t min_saved) {
+  // Forking saves the prefix tokens a rescan scans more than once and costs
+  // one launch per level beyond the first.
+  const int64_t saved = p.path_tokens - p.n_tokens;
+  const int64_t extra = p.n_levels - 1;
+  if (!p.paths_ok || extra == 0) return TREE_SCHED_LEVEL;
+  const bool fork = min_saved == 0 || saved / extra >= min_saved;
+  return fork ? TREE_SCHED_LEVEL : TREE_SCHED_RESCAN;
+}
+
 int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
                int32_t conv_width, Plan* out, std::string* err) {
   if (!parents || !seg_lens || !out) {
@@ -129,6 +139,36 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
     tail(i, p.ctx_src.data() + static_cast<size_t>(i) * H);
   }
 
+  // Rescan walks (the fork-free alternative of the tree-recurrence 0.1.0
+  // project page, "How a tree runs": every root-to-leaf path is scanned
+  // whole, and each segment keeps the outputs of one path through it).
+  // A segment is owned by the lowest-indexed leaf below it: walking the
+  // segments backwards, a leaf owns itself and a parent takes the smallest
+  // owner among its children.
+  for (int32_t i = 0; i < n_seg; ++i)
+    if (n_children[i] == 0) p.path_entries += p.depth[i] + 1;
+  p.paths_ok = p.path_entries <= Plan::kMaxPathEntries;
+  if (p.paths_ok) {
+    std::vector<int32_t> owner(n_seg, n_seg), leaves;
+    for (int32_t i = n_seg - 1; i >= 0; --i) {
+      if (n_children[i] == 0) owner[i] = i;
+      if (p.parents[i] >= 0) owner[p.parents[i]] = std::min(owner[p.parents[i]], owner[i]);
+    }
+    for (int32_t i = 0; i < n_seg; ++i)
+      if (n_children[i] == 0) leaves.push_back(i);
+    std::stable_sort(leaves.begin(), leaves.end(),
+                     [&](int32_t a, int32_t b) { return path_len[a] > path_len[b]; });
+    p.path_off.assign(1, 0);
+    p.path_seg.reserve(static_cast<size_t>(p.path_entries));
+    std::vector<int32_t> up;
+    for (const int32_t leaf : leaves) {
+      up.clear();
+      for (int32_t s = leaf; s >= 0; s = p.parents[s]) up.push_back(s);
+      for (auto it = up.rbegin(); it != up.rend(); ++it) p.path_seg.push_back(owner[*it] == leaf ? *it : ~*it);
+      p.path_off.push_back(static_cast<int32_t>(p.path_seg.size()));
+    }
+  }
+
   // Device mirror.
   p.m_seg_off = 0;
   p.m_parent = p.m_seg_off + n_seg + 1;
@@ -137,7 +177,9 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   p.m_order = p.m_hist + p.hist.size();
   p.m_root = p.m_order + n_seg;
   p.m_ctx = p.m_root + n_seg;
-  p.mirror.resize(p.m_ctx + p.ctx_src.size());
+  p.m_path_off = p.m_ctx + p.ctx_src.size();
+  p.m_path_seg = p.m_path_off + p.path_off.size();
+  p.mirror.resize(p.m_path_seg + p.path_seg.size());
   std::copy(p.seg_off.begin(), p.seg_off.end(), p.mirror.begin() + p.m_seg_off);
   std::copy(p.parents.begin(), p.parents.end(), p.mirror.begin() + p.m_parent);
   std::copy(p.slot.begin(), p.slot.end(), p.mirror.begin() + p.m_slot);
@@ -145,6 +187,8 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   std::copy(p.order.begin(), p.order.end(), p.mirror.begin() + p.m_order);
   std::copy(p.root_idx.begin(), p.root_idx.end(), p.mirror.begin() + p.m_root);
   std::copy(p.ctx_src.begin(), p.ctx_src.end(), p.mirror.begin() + p.m_ctx);
+  std::copy(p.path_off.begin(), p.path_off.end(), p.mirror.begin() + p.m_path_off);
+  std::copy(p.path_seg.begin(), p.path_seg.end(), p.mirror.begin() + p.m_path_seg);
 
   *out = std::move(p);
   return TREE_OK;

@@ -36,12 +36,28 @@ struct Plan {
   std::vector<int32_t> level_start;  // n_levels + 1
   std::vector<int32_t> order;        // segments by (level, length desc, index)
 
+  // Rescan walks: one per leaf, longest path first (ties by leaf index).
+  // Walk w is entries path_seg[path_off[w] .. path_off[w+1]-1], the segments
+  // of the leaf's root path from the root down; an entry is the segment
+  // index when this walk owns the segment's outputs and state (the walk of
+  // the lowest-indexed leaf below it), its bitwise complement otherwise.
+  // Empty (and paths_ok false) when the table would exceed kMaxPathEntries.
+  static constexpr int64_t kMaxPathEntries = int64_t(1) << 26;
+  bool paths_ok = false;
+  int64_t path_entries = 0;  // sum over leaves of (depth + 1)
+  std::vector<int32_t> path_off, path_seg;
+
   // Device copy: one int32 array; element offsets of each table inside it.
   std::vector<int32_t> mirror;
   size_t m_seg_off = 0, m_parent = 0, m_slot = 0, m_hist = 0, m_order = 0, m_root = 0, m_ctx = 0;
+  size_t m_path_off = 0, m_path_seg = 0;
 
   size_t device_bytes() const { return mirror.size() * sizeof(int32_t); }
 };
+
+// The fork/rescan choice (TREE_SCHED_LEVEL or TREE_SCHED_RESCAN) for a
+// launch priced at `min_saved` scanned tokens (>= 0).
+int32_t choose_schedule(const Plan& p, int64_t min_saved);
 
 // Returns 0 or a negative TREE_ERR_* code; on failure *err holds a message.
 int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,

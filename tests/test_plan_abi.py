@@ -172,3 +172,69 @@ def test_library_shares_torchs_hip_runtime():
     maps = open("/proc/self/maps").read()
     hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
     assert len(hip) == 1, hip
+
+
+# ------------------------------------------------------------ rescan walks
+
+def _decode(e):
+    return (int(e), True) if e >= 0 else (int(~e), False)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_rescan_walks_are_the_leaf_paths_with_one_owner_each(seed):
+    rng = np.random.default_rng(30 + seed)
+    parents, lens = rand_trie(rng, 60, 40, n_roots=1 + seed)
+    plan = _lib.TreePlan(parents, lens, 4)
+    off, seg = plan.paths()
+    walks = [[_decode(e) for e in seg[off[w]:off[w + 1]]] for w in range(len(off) - 1)]
+    want = {tuple(p) for p in otrie.leaf_paths(parents)}
+    assert {tuple(s for s, _ in w) for w in walks} == want and len(walks) == len(want)
+    assert plan.stats["path_entries"] == sum(len(p) for p in want)
+    plen = [sum(int(lens[s]) for s, _ in w) for w in walks]
+    assert all(a >= b for a, b in zip(plen, plen[1:])), "longest walk first"
+    owners = {}
+    for w, walk in enumerate(walks):
+        for s, own in walk:
+            if own:
+                assert s not in owners, f"segment {s} written twice"
+                owners[s] = walk[-1][0]
+    assert sorted(owners) == list(range(len(parents)))
+    # The owner is the lowest-indexed leaf whose root path holds the segment.
+    for s in range(len(parents)):
+        assert owners[s] == min(p[-1] for p in want if s in p)
+
+
+def _expected_schedule(parents, lens, t):
+    saved = otrie.path_token_count(parents, lens) - int(np.sum(lens))
+    depth = np.zeros(len(parents), int)
+    for i, p in enumerate(parents):
+        depth[i] = 0 if p < 0 else depth[p] + 1
+    extra = int(depth.max())
+    return "level" if extra == 0 or saved >= t * extra else "rescan"
+
+
+def test_fork_rescan_policy():
+    rng = np.random.default_rng(7)
+    cases = [(np.array([-1, 0, 1, 2], np.int32), np.array([50, 9, 70, 3], np.int32)),  # chain
+             (np.array([-1, -1, -1], np.int32), np.array([5, 6, 7], np.int32)),          # forest
+             (np.array([-1, 0, 0], np.int32), np.array([1000, 10, 10], np.int32))]       # fork
+    cases += [rand_trie(rng, 30, 200, n_roots=2) for _ in range(4)]
+    cases += [make_trie(c)[:2] for c in sorted(CONFIGS)]
+    for parents, lens in cases:
+        plan = _lib.TreePlan(parents, lens, 4)
+        for t in (0, 1, 10, 999, 1000, 1001, 4096, 1 << 20, 1 << 40):
+            assert plan.choose_schedule(t) == _expected_schedule(parents, lens, t), (parents, t)
+    chain = _lib.TreePlan([-1, 0, 1], [10, 10, 10], 4)
+    assert chain.choose_schedule(1) == "rescan" and chain.choose_schedule(0) == "level"
+    lib = _lib.load()
+    out = ctypes.c_int32()
+    assert lib.tree_plan_choose_schedule(chain.handle, -1, ctypes.byref(out)) == -1
+
+
+def test_schedule_constants_match_the_header():
+    text = open(HEADER).read()
+    val = lambda name: int(re.search(rf"#define {name}\s+\(?(-?\d+)", text).group(1))  # noqa: E731
+    assert val("TREE_SCHED_LEVEL") == _lib.SCHED_LEVEL
+    assert val("TREE_SCHED_RESCAN") == _lib.SCHED_RESCAN
+    assert val("TREE_SCHED_AUTO") == _lib.SCHED_AUTO
+    assert val("TREE_FORK_MIN_SAVED_TOKENS") == _lib.FORK_MIN_SAVED_TOKENS
