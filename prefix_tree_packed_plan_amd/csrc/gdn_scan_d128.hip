@@ -51,6 +51,8 @@
 // LDS bank once per half-wave.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "../../include/tree_gdn.h"
 #include "launch.hpp"
 
@@ -120,6 +122,16 @@ __device__ __forceinline__ float dpp_shr(float x, int n) {
   }
 }
 // Sum over the 4 lanes of a quad (lanes 4k..4k+3), result in all four.
+// f(integral_constant<int, M>) for M in order (compile-time step indices).
+template <typename F, int... M>
+__device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int, M...>) {
+  (f(std::integral_constant<int, M>{}), ...);
+}
+// Lane k of each quad, broadcast to the whole quad (DPP quad_perm [k,k,k,k]).
+template <int K>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), K * 0x55, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float quad_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
@@ -370,54 +382,53 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     // -- prep
     if (cw < 2) {
       // Diagonal block cw: A[i][j] = b_i exp(G_i - G_j) k_i.k_j (j < i) and
-      // T = (I + A)^-1 by fp32 forward substitution, lane (j, p) =
-      // (lane/4, lane%4) owning column j and the terms m = 4q + p of every
-      // row sum, so a step is <= 4 FMAs and a quad sum.
+      // T = (I + A)^-1 by right-looking fp32 substitution: once row m of T
+      // is final, every row r > m subtracts A[r][m] T[m][:].  Lane (j, p) =
+      // (lane/4, lane%4) holds T[4q + p][j] in t[q]; row m is broadcast
+      // from the quad lane that owns it, so a step is one DPP move and up to
+      // 4 independent FMAs (no reduction on the dependency chain).
+      // -A is stored by columns: abb[m][p][3 - q] = -A[4q + p][m], so step m
+      // reads the 4 - m/4 rows it updates as one contiguous piece.
       const f32x4 d = gram(Ks + ROW16 * cw, Ks + ROW16 * cw, ao);  // lane i, rows j
       {
         const float gi = gtw[16 * cw + i16];
         const float bi = gtw[2 * CH + 16 * cw + i16];
         const f32x4 gj = *reinterpret_cast<const f32x4*>(&gtw[16 * cw + 4 * h4]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sm.abb[cw][i16 * 16 + r * 4 + h4] = 4 * h4 + r < i16 ? bi * d[r] * ex2(gi - gj[r]) : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int m = 4 * h4 + r;
+          sm.abb[cw][m * 16 + (i16 & 3) * 4 + 3 - (i16 >> 2)] = m < i16 ? -bi * d[r] * ex2(gi - gj[r]) : 0.f;
+        }
       }
       asm volatile("" ::: "memory");
       const int jc = lane >> 2, ph = lane & 3;
-      // Row rr needs the terms q < ceil(rr / 4) only.
-      float arow[16][4];
+      float na[15][4];  // na[m][3 - q] = -A[4q + ph][m], for q >= m / 4
 #pragma unroll
-      for (int rr = 1; rr < 16; ++rr) {
-        const float* pa = &sm.abb[cw][rr * 16 + ph * 4];
-        if (rr <= 4) {
-          arow[rr][0] = pa[0];
-        } else if (rr <= 8) {
-          const float2 v = *reinterpret_cast<const float2*>(pa);
-          arow[rr][0] = v.x, arow[rr][1] = v.y;
-        } else {
+      for (int m = 0; m < 15; ++m) {
+        const float* pa = &sm.abb[cw][m * 16 + ph * 4];
+        if (m < 4) {
           const float4 v = *reinterpret_cast<const float4*>(pa);
-          arow[rr][0] = v.x, arow[rr][1] = v.y, arow[rr][2] = v.z, arow[rr][3] = v.w;
+          na[m][0] = v.x, na[m][1] = v.y, na[m][2] = v.z, na[m][3] = v.w;
+        } else if (m < 8) {
+          const float2 v = *reinterpret_cast<const float2*>(pa);
+          na[m][0] = v.x, na[m][1] = v.y, na[m][2] = pa[2];
+        } else if (m < 12) {
+          const float2 v = *reinterpret_cast<const float2*>(pa);
+          na[m][0] = v.x, na[m][1] = v.y;
+        } else {
+          na[m][0] = pa[0];
         }
       }
-      // T[r][jc] = delta(r, jc) - sum_{m<r} A[r][m] T[m][jc] for every r:
-      // starting from the identity, rows above the diagonal stay zero by
-      // themselves.  Lane phase ph owns rows r = 4q + ph; w[p] = (p == ph)
-      // selects the lanes that own row r.
-      float t[4], w[4];
+      float t[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        t[q] = 4 * q + ph == jc ? 1.f : 0.f;
-        w[q] = q == ph ? 1.f : 0.f;
-      }
+      for (int q = 0; q < 4; ++q) t[q] = 4 * q + ph == jc ? 1.f : 0.f;
+      auto step = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const float bc = quad_bcast<m & 3>(t[m >> 2]);  // T[m][jc]
 #pragma unroll
-      for (int rr = 1; rr < 16; ++rr) {
-        // A is strictly lower (zeros from the gated tile), so terms with
-        // 4q + ph >= rr read zeros and need no mask.
-        float part = 0.f;
-#pragma unroll
-        for (int q = 0; 4 * q < rr; ++q) part += arow[rr][q] * t[q];
-        t[rr >> 2] -= w[rr & 3] * quad_sum(part);
-      }
+        for (int q = m >> 2; q < 4; ++q) t[q] = fmaf(na[m][3 - q], bc, t[q]);
+      };
+      for_each_index(step, std::make_integer_sequence<int, 15>{});
       // T[4q + ph][jc] -> operand lane (row 4q + ph, group jc / 4), element jc % 4.
       uint16_t* tt = reinterpret_cast<uint16_t*>(&sm.ttab[cw][0]);
 #pragma unroll
