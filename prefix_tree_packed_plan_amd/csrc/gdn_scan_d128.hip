@@ -17,10 +17,13 @@
 // their phases drift apart, so one's MFMA work fills the other's latency.
 // Per chunk:
 //
-//   prep (no state needed)   every wave: its own copy of the gate prefix
-//                            (DPP scan).  Waves 0 and 1: one 16 x 16 diagonal
-//                            block of K K^T each and its inverse (I + A_bb)^-1
-//                            (fp32 forward substitution).  Wave 2: the
+//   gates                    made for the next chunk by one wave (GW) in its
+//                            slack before the chunk barrier: the in-chunk
+//                            prefix G (DPP scan) and the tables every wave
+//                            reads, double-buffered in LDS.
+//   prep (no state needed)   Waves 0 and 1: one 16 x 16 diagonal block of
+//                            K K^T each and its inverse (I + A_bb)^-1 (fp32
+//                            right-looking substitution).  Wave 2: the
 //                            off-diagonal block A_10.  Waves 3, 6, 7: the three
 //                            Q K^T blocks.  All land in LDS as ready-made MFMA
 //                            operands, split hi + lo where they feed the state.
@@ -46,7 +49,7 @@
 // instruction each) at a 1088-byte stride, block b shifted by a further
 // {0, 2, 1, 3}[b % 4] x 16 bytes, and the 16-byte chunk c of row r stored at
 // slot c ^ 4(r % 4).  With it the two read patterns used here -- MFMA operand
-// reads (two 8-byte pieces 32 bytes apart, one ds_read2_b64) of 16 rows and
+// reads (two 8-byte pieces 32 bytes apart, two ds_read_b64) of 16 rows and
 // the transposing read ds_read_b64_tr_b16 of 4 rows x 16 columns -- hit every
 // LDS bank once per half-wave.
 #include <hip/hip_runtime.h>
@@ -73,6 +76,7 @@ typedef __attribute__((address_space(3))) const u32x2 lds_u2;
 constexpr int CH = 32;          // chunk length (tokens)
 constexpr int D = 128;          // d_k = d_v
 constexpr int NW = 8;           // waves per work-group
+constexpr int GW = 3;           // the wave that loads g, beta and makes the gate tables
 constexpr int TSZ = 8704;       // LDS bytes of one 32 x 128 bf16 tile (see toff)
 constexpr int ROW16 = 4352;     // bytes between rows 16 apart
 constexpr float kLog2e = 1.4426950408889634f;
@@ -177,9 +181,10 @@ struct Smem {
   alignas(16) uint4 ttab[3][64];
   // 16x16x32 B operands of O^T += U^T P^T for token blocks 0 and 1.
   alignas(16) uint4 ptab[2][64];
-  // Waves 0, 1: their gated diagonal block, A[r][4q + p] at [r][p][q].
+  // Waves 0, 1: their gated diagonal block by columns, -A[4q + p][m] at [m][p][3 - q].
   alignas(16) float abb[2][256];
-  alignas(16) float gt[NW][4][CH];   // per wave: G log2(e), exp(G), beta, exp(G_L - G)
+  // Gate tables of the chunk in buffer s: G log2(e), exp(G), beta, exp(G_L - G).
+  alignas(16) float gt[2][4][CH];
   alignas(16) float graw[2][CH];
   alignas(16) float braw[2][CH];
   // Output rows of the previous chunk, 256 bytes per token, 16-byte chunk c
@@ -260,7 +265,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   const uint16_t* vg = static_cast<const uint16_t*>(args.v);
   uint16_t* og = static_cast<uint16_t*>(args.o);
   const int col_w = 16 * cw;
-  float* gtw = &sm.gt[cw][0][0];  // this wave's gate tables
 
   // Loop-constant byte offsets of the hot reads: operand reads of rows i16
   // (+16 per row block) at columns 32kk + 4h4; transposing reads of K at
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   }
 
   // Chunk at token tc into buffer buf: wave cw loads block cw (rows
-  // 4cw..4cw+3) of the K, Q and V tiles; waves 4 and 5 the gate rows.  In a
+  // 4cw..4cw+3) of the K, Q and V tiles; wave GW the g and beta rows.  In a
   // partial chunk, rows past the end repeat row Ln - 1.
   auto fetch = [&](int tc, int end, int buf) {
     // Offsets of once-per-chunk accesses are recomputed from an opaque copy
@@ -314,11 +318,35 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sm.kb[buf] + lo), 16, ok, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sm.qb[buf] + lo), 16, ok, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sm.vb[buf] + lo), 16, ov, 0, 0, 0);
-    if ((cw == 4 || cw == 5) && lane < CH) {  // lane l writes LDS word l of the row
-      const float* src = (cw == 5 ? args.beta : args.g) + static_cast<size_t>(tc) * args.h_v + h;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(src, CH * args.h_v * 4),
-                                               (lds_void*)(cw == 5 ? sm.braw[buf] : sm.graw[buf]), 4,
-                                               min(lane, Ln - 1) * args.h_v * 4, 0, 0, 0);
+    if (cw == GW && lane < CH) {  // lane l writes LDS word l of the row
+      const size_t base = static_cast<size_t>(tc) * args.h_v + h;
+      const int go = min(lane, Ln - 1) * args.h_v * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(args.g + base, CH * args.h_v * 4), (lds_void*)sm.graw[buf], 4, go,
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(args.beta + base, CH * args.h_v * 4), (lds_void*)sm.braw[buf], 4,
+                                               go, 0, 0, 0);
+    }
+  };
+
+  // Gate tables of the chunk in buffer buf (L tokens), by wave GW once its
+  // own DMA of g and beta has landed: inclusive prefix G of g over rows of
+  // 16 lanes (DPP), then row 1 adds row 0's total.
+  auto make_gates = [&](int buf, int L) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    float x = lane < L ? sm.graw[buf][lane & (CH - 1)] : 0.f;
+    x += dpp_shr(x, 1);
+    x += dpp_shr(x, 2);
+    x += dpp_shr(x, 4);
+    x += dpp_shr(x, 8);
+    x += lane >= 16 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15)) : 0.f;
+    const float g2 = x * kLog2e;
+    const float g2L = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), CH - 1));
+    if (lane < CH) {
+      float* gt = &sm.gt[buf][0][0];
+      gt[lane] = g2;
+      gt[CH + lane] = ex2(g2);
+      gt[2 * CH + lane] = lane < L ? sm.braw[buf][lane] : 0.f;
+      gt[3 * CH + lane] = ex2(g2L - g2);
     }
   };
 
@@ -335,6 +363,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   };
 
   fetch(seg_beg, seg_end, 0);
+  if (cw == GW) make_gates(0, min(CH, seg_end - seg_beg));
   int s = 0;
   int prev_t0 = -1, prev_L = 0;
   bool prev_own = true;
@@ -358,26 +387,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of the chunk has landed
     __syncthreads();                                   // (A) ... and every other wave's
     if (more) fetch(nt0, nend, s ^ 1);
+    // The previous chunk's output rows leave right after the next chunk's
+    // DMA is issued (not ahead of it), a whole chunk before the wait above
+    // has to count them.
+    if (prev_t0 >= 0 && prev_own) store_out(prev_t0, prev_L);
 
-    // -- gates, per wave: inclusive prefix of g over rows of 16 lanes (DPP),
-    //    then row 1 adds row 0's total
-    {
-      float x = lane < Lc ? sm.graw[s][lane & (CH - 1)] : 0.f;
-      x += dpp_shr(x, 1);
-      x += dpp_shr(x, 2);
-      x += dpp_shr(x, 4);
-      x += dpp_shr(x, 8);
-      x += lane >= 16 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15)) : 0.f;
-      const float g2 = x * kLog2e;
-      const float g2L = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), CH - 1));
-      if (lane < CH) {
-        gtw[lane] = g2;
-        gtw[CH + lane] = ex2(g2);
-        gtw[2 * CH + lane] = lane < Lc ? sm.braw[s][lane] : 0.f;
-        gtw[3 * CH + lane] = ex2(g2L - g2);
-      }
-    }
-    asm volatile("" ::: "memory");
+    // -- gate tables of this chunk (made by wave GW during the previous one)
+    const float* gtw = &sm.gt[s][0][0];
 
     // -- prep
     if (cw < 2) {
@@ -495,9 +511,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       R[b] = bv * (vv - gv * R[b]);
       OT[b] *= args.scale * gtw[CH + 16 * b + i16];
     }
-    // The previous chunk's output rows leave here, after the next chunk's
-    // DMA has been issued, so they do not queue ahead of it.
-    if (prev_t0 >= 0 && prev_own) store_out(prev_t0, prev_L);
     __syncthreads();  // (D) the inverse, -A and P^T operands of every wave are in LDS
 
     // -- state, part 2: block solve, output and state update
@@ -559,6 +572,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       if (more) own = args.walk[++wj] >= 0;
     }
     if (!more) break;
+    // The next chunk's gate tables, in this wave's slack before barrier A.
+    if (cw == GW) make_gates(s ^ 1, min(CH, nend - nt0));
     t0 = nt0;
     seg_end = nend;
     seg = nseg;
