@@ -77,6 +77,7 @@ constexpr int CH = 32;          // chunk length (tokens)
 constexpr int D = 128;          // d_k = d_v
 constexpr int NW = 8;           // waves per work-group
 constexpr int GW = 3;           // the wave that loads g, beta and makes the gate tables
+constexpr int DW0 = 4;          // waves DW0, DW0 + 1 DMA the q, k, v tiles and store the output (16 rows each)
 constexpr int TSZ = 8704;       // LDS bytes of one 32 x 128 bf16 tile (see toff)
 constexpr int ROW16 = 4352;     // bytes between rows 16 apart
 constexpr float kLog2e = 1.4426950408889634f;
@@ -299,8 +300,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
   }
 
-  // Chunk at token tc into buffer buf: wave cw loads block cw (rows
-  // 4cw..4cw+3) of the K, Q and V tiles; wave GW the g and beta rows.  In a
+  // Chunk at token tc into buffer buf: waves DW0 and DW0 + 1, which have the
+  // least work before the chunk barrier, load row blocks 0-3 and 4-7 (rows
+  // 4b..4b+3) of the K, Q and V tiles; wave GW the g and beta rows.  In a
   // partial chunk, rows past the end repeat row Ln - 1.
   auto fetch = [&](int tc, int end, int buf) {
     // Offsets of once-per-chunk accesses are recomputed from an opaque copy
@@ -312,12 +314,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     const auto rk = rsrc(kg + (static_cast<size_t>(tc) * args.h_qk + hq) * D, CH * rs_qk);
     const auto rq = rsrc(qg + (static_cast<size_t>(tc) * args.h_qk + hq) * D, CH * rs_qk);
     const auto rv = rsrc(vg + (static_cast<size_t>(tc) * args.h_v + h) * D, CH * rs_v);
-    const int row = min(4 * cw + (ln >> 4), Ln - 1);  // block cw of each tile
-    const int ok = row * rs_qk + cofs, ov = row * rs_v + cofs;
-    const int lo = blk_off(cw);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sm.kb[buf] + lo), 16, ok, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sm.qb[buf] + lo), 16, ok, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sm.vb[buf] + lo), 16, ov, 0, 0, 0);
+    if (cw == DW0 || cw == DW0 + 1) {
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const int blk = 4 * (cw - DW0) + bi;
+        const int row = min(4 * blk + (ln >> 4), Ln - 1);
+        const int ok = row * rs_qk + cofs, ov = row * rs_v + cofs;
+        const int lo = blk_off(blk);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sm.kb[buf] + lo), 16, ok, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sm.qb[buf] + lo), 16, ok, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sm.vb[buf] + lo), 16, ov, 0, 0, 0);
+      }
+    }
     if (cw == GW && lane < CH) {  // lane l writes LDS word l of the row
       const size_t base = static_cast<size_t>(tc) * args.h_v + h;
       const int go = min(lane, Ln - 1) * args.h_v * 4;
@@ -350,16 +358,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     }
   };
 
-  // Whole token rows of the staged output; the descriptor ends after row
-  // Ln - 1, so rows past it are not written.
-  // This lane stores 16-byte chunk lane % 16 of token row 4cw + lane / 16.
+  // Whole token rows of the staged output, by the DMA waves (rows 16(cw -
+  // DW0) .. +15); the descriptor ends after row Ln - 1, so rows past it are
+  // not written.  A lane stores 16-byte chunk lane % 16 of token rows
+  // 4b + lane / 16.
   auto store_out = [&](int tc, int Ln) {
+    if (cw != DW0 && cw != DW0 + 1) return;
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    const int orow = 4 * cw + (ln >> 4);
     const auto ro = rsrc(og + (static_cast<size_t>(tc) * args.h_v + h) * D, (Ln - 1) * rs_v + D * 2);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(sm.ost + orow * 256 + 16 * ((ln & 15) ^ (orow & 15)));
-    __builtin_amdgcn_raw_buffer_store_b128(v, ro, orow * rs_v + 16 * (ln & 15), 0, 0);
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+      const int orow = 4 * (4 * (cw - DW0) + bi) + (ln >> 4);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sm.ost + orow * 256 + 16 * ((ln & 15) ^ (orow & 15)));
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, orow * rs_v + 16 * (ln & 15), 0, 0);
+    }
   };
 
   fetch(seg_beg, seg_end, 0);
