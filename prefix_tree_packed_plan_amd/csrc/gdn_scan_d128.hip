@@ -154,15 +154,12 @@ __device__ __forceinline__ int toff(int row, int col) {
 // col0 + kmap(h, 0..7), kmap(h, j) = j<4 ? 4h+j : 16+4h+(j-4); the two 8-byte
 // pieces are 32 bytes apart in this layout.  The same K order lets two
 // accumulator tiles (rows 4h..4h+3 of each) serve as one K = 32 operand
-// without moving data.  The second address is hidden from the compiler so
-// that the pieces stay two ds_read_b64: fused into one ds_read2_b64 they
-// take several times as long on this part.
-__device__ __forceinline__ uint4 ld_a8(const char* t, int o) {
-  const lds_u2* p0 = (const lds_u2*)(t + o);
-  uint32_t a1 = static_cast<uint32_t>((uintptr_t)p0) + 32;
-  asm volatile("" : "+v"(a1));
-  const lds_u2* p1 = (const lds_u2*)(uintptr_t)a1;
-  const u32x2 x = *p0, y = *p1;
+// without moving data.  The second piece is read at `o2`, a loop-constant
+// copy of o + 32 that the compiler cannot see through, so the pieces stay
+// two ds_read_b64 (fused into one ds_read2_b64 they take several times as
+// long on this part) and each address is one register plus an immediate.
+__device__ __forceinline__ uint4 ld_a8(const char* t, int o, int o2) {
+  const u32x2 x = *(const lds_u2*)(t + o), y = *(const lds_u2*)(t + o2);
   return make_uint4(x[0], x[1], y[0], y[1]);
 }
 // Transposing read at byte offset `o` = toff(row0 + 4h + i/4, col0 + 4(i%4))
@@ -200,13 +197,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 
 // Raw 16 x 16 Gram tile D[x][y] = X[x] . Y[y] over 128 features (X, Y point
 // at row blocks of tiles): lane (y = i, h) holds x = 4h + 0..3.
-// ao[kk] = toff(i, 32kk + 4h).
-__device__ __forceinline__ f32x4 gram(const char* X, const char* Y, const int* ao) {
+// ao[kk] = toff(i, 32kk + 4h), ao2[kk] its opaque copy + 32.
+__device__ __forceinline__ f32x4 gram(const char* X, const char* Y, const int* ao, const int* ao2) {
   uint4 a[4], b[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    a[kk] = ld_a8(X, ao[kk]);
-    b[kk] = ld_a8(Y, ao[kk]);
+    a[kk] = ld_a8(X, ao[kk], ao2[kk]);
+    b[kk] = ld_a8(Y, ao[kk], ao2[kk]);
   }
   f32x4 acc = zero4();
 #pragma unroll
@@ -270,10 +267,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   // Loop-constant byte offsets of the hot reads: operand reads of rows i16
   // (+16 per row block) at columns 32kk + 4h4; transposing reads of K at
   // columns 32m (+16 is +32 bytes) and of V at this wave's columns.
-  int ao[4], ko[4];
+  int ao[4], ao2[4], ko[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     ao[kk] = toff(i16, 32 * kk + 4 * h4);
+    ao2[kk] = ao[kk] + 32;
+    asm volatile("" : "+v"(ao2[kk]));
     ko[kk] = toff(4 * h4 + (i16 >> 2), 32 * kk + 4 * (i16 & 3));
   }
   const int vo = toff(4 * h4 + (i16 >> 2), col_w + 4 * (i16 & 3));
@@ -418,7 +417,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       // 4 independent FMAs (no reduction on the dependency chain).
       // -A is stored by columns: abb[m][p][3 - q] = -A[4q + p][m], so step m
       // reads the 4 - m/4 rows it updates as one contiguous piece.
-      const f32x4 d = gram(Ks + ROW16 * cw, Ks + ROW16 * cw, ao);  // lane i, rows j
+      const f32x4 d = gram(Ks + ROW16 * cw, Ks + ROW16 * cw, ao, ao2);  // lane i, rows j
       {
         const float gi = gtw[16 * cw + i16];
         const float bi = gtw[2 * CH + 16 * cw + i16];
@@ -470,7 +469,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     } else if (cw == 2) {
       // -A_10 as the A operand of R_1 -= A_10 U_0: lane i (token 16 + i),
       // rows j (tokens 0..15).
-      const f32x4 d = gram(Ks, Ks + ROW16, ao);
+      const f32x4 d = gram(Ks, Ks + ROW16, ao, ao2);
       const float gi = gtw[16 + i16];
       const float bi = gtw[2 * CH + 16 + i16];
       const f32x4 gj = *reinterpret_cast<const f32x4*>(&gtw[4 * h4]);
@@ -483,7 +482,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     } else if (cw == 3 || cw >= 6) {
       // P^T block (jb, ib) = (0, 0), (0, 1), (1, 1): lane i (query), rows j (key).
       const int jb = cw == 7 ? 1 : 0, ib = cw == 3 ? 0 : 1;
-      const f32x4 d = gram(Ks + ROW16 * jb, Qs + ROW16 * ib, ao);
+      const f32x4 d = gram(Ks + ROW16 * jb, Qs + ROW16 * ib, ao, ao2);
       const float gi = gtw[16 * ib + i16];
       const f32x4 gj = *reinterpret_cast<const f32x4*>(&gtw[16 * jb + 4 * h4]);
       f32x4 v;
@@ -509,8 +508,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       S[2 * kk + 1] *= gL;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const uint4 ak = ld_a8(Ks + ROW16 * b, ao[kk]);
-        const uint4 aq = ld_a8(Qs + ROW16 * b, ao[kk]);
+        const uint4 ak = ld_a8(Ks + ROW16 * b, ao[kk], ao2[kk]);
+        const uint4 aq = ld_a8(Qs + ROW16 * b, ao[kk], ao2[kk]);
         R[b] = mma32(ak, sh, R[b]);
         R[b] = mma32(ak, sl, R[b]);
         OT[b] = mma32(sh, aq, OT[b]);
