@@ -217,6 +217,46 @@ int tree_conv(const void* x, const void* w, const void* bias, void* y, const voi
               const tree_plan_t* plan, const void* dplan, void* stream);
 
 /*
+ * tree_conv_backward_workspace_bytes -- device workspace tree_conv_backward
+ * needs for `channels`: the dz of every segment's first W-1 tokens and the
+ * per-block partial sums of dw and dbias, fp32.
+ */
+size_t tree_conv_backward_workspace_bytes(const tree_plan_t* plan, int32_t channels);
+
+/*
+ * tree_conv_backward -- gradients of the tree conv ("Tree Training"
+ * section 3.2 Eq. 11; the backward of the per-path definition, section 3.1
+ * Eq. 6, each token's output counted once).  With z the pre-activation and
+ * dz = dy * act'(z):
+ *
+ *   dx[j, c]   = sum_{d=0}^{W-1} w[c, W-1-d] * sum of dz[t, c] over the tokens
+ *                t that lie d steps after j on some root-to-leaf path,
+ *   dw[c, i]   = sum_t dz[t, c] * xin(t, i - (W-1), c),
+ *   dbias[c]   = sum_t dz[t, c],
+ *   dinit_ctx  = the same gradient for the roots' given context rows.
+ *
+ * Past the end of its segment a token's successors are the first tokens of
+ * every child (and deeper, for children shorter than W-1): a parent's last
+ * W-1 inputs receive the sum over all children (same paper, section 3.2 and
+ * appendix A.2, sibling gradients accumulate in what the parent hands them;
+ * appendix B.7, fp32 accumulation).  Sums run in a fixed order: the result
+ * is deterministic.
+ *
+ * x, w, bias, init_ctx   the forward's inputs (bias, init_ctx may be NULL).
+ * dy        device, [n_tokens, channels], dtype       (read)
+ * dx        device, [n_tokens, channels], dtype       (written)
+ * dw        device, [channels, W] fp32                (written)
+ * dbias     device, [channels] fp32, or NULL          (written)
+ * dinit_ctx device, [n_roots, W-1, channels] fp32, or NULL (written; W > 1)
+ * ws        device workspace of ws_bytes >= tree_conv_backward_workspace_bytes.
+ * Errors: INVALID_ARG, SIZE, UNSUPPORTED (W > 4), WORKSPACE, HIP.
+ */
+int tree_conv_backward(const void* x, const void* w, const void* bias, const void* dy, const void* init_ctx,
+                       void* dx, float* dw, float* dbias, float* dinit_ctx, int64_t n_tokens, int32_t channels,
+                       int32_t dtype, int32_t act, const tree_plan_t* plan, const void* dplan, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
  * tree_scan_workspace_bytes -- device workspace tree_gdn_scan needs under
  * TREE_SCHED_LEVEL (or AUTO): one fp32 state [h_v, d_k, d_v] per segment with
  * children (0 when the caller passes `states`, which then carries the parent

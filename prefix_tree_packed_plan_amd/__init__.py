@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     TreePlan,
     load,
     tree_conv,
+    tree_conv_backward,
     tree_gdn_scan,
     tree_plan,
 )

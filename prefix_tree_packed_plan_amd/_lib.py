@@ -62,6 +62,9 @@ SIGNATURES = {
     "tree_plan_device_bytes": (_SZ, [_P]),
     "tree_plan_upload": (ctypes.c_int, [_P, _P, _SZ, _P]),
     "tree_conv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]),
+    "tree_conv_backward_workspace_bytes": (_SZ, [_P, _I32]),
+    "tree_conv_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
+                                          _SZ, _P]),
     "tree_scan_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
     "tree_gdn_scan": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
                                      _F, _I32, _I32, _P, _P, _P, _SZ, _P]),
@@ -262,6 +265,47 @@ def tree_conv(x, w, plan: TreePlan, bias=None, act: Optional[str] = None, out=No
     if return_ctx:
         return y, ctx_out
     return y
+
+
+def tree_conv_backward(x, w, dy, plan: TreePlan, bias=None, act: Optional[str] = None, init_ctx=None,
+                       dx=None, workspace=None):
+    """Gradients of the tree conv: (dx [N, C] in x's dtype, dw [C, W] fp32,
+    dbias [C] fp32 or None, dinit_ctx [n_roots, W-1, C] fp32 or None).
+    dy is the gradient of the conv output (same dtype as x)."""
+    import torch
+    _need(x, "x")
+    dev = x.device
+    _need(w, "w", x.dtype, dev)
+    _need(dy, "dy", x.dtype, dev)
+    if x.dim() != 2 or dy.shape != x.shape or w.dim() != 2 or w.shape[0] != x.shape[1]:
+        raise ValueError("shapes must be x, dy [N, C] and w [C, W]")
+    n, c = x.shape
+    w1 = w.shape[1] - 1
+    if w.shape[1] != plan.conv_width:
+        raise ValueError("w's width must be the plan's conv width")
+    if bias is not None:
+        _need(bias, "bias", x.dtype, dev)
+    if init_ctx is not None:
+        _need(init_ctx, "init_ctx", x.dtype, dev)
+        if tuple(init_ctx.shape) != (plan.n_roots, w1, c):
+            raise ValueError("init_ctx must be [n_roots, W-1, C]")
+    dx = torch.empty_like(x) if dx is None else dx
+    _need(dx, "dx", x.dtype, dev)
+    dw = torch.empty((c, w1 + 1), dtype=torch.float32, device=dev)
+    db = torch.empty(c, dtype=torch.float32, device=dev) if bias is not None else None
+    dctx = torch.empty((plan.n_roots, w1, c), dtype=torch.float32, device=dev) if w1 > 0 else None
+    lib = load()
+    need = int(lib.tree_conv_backward_workspace_bytes(plan.handle, c))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    a = {None: ACT_NONE, "silu": ACT_SILU}[act]
+    dplan = plan.on_device(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    _check(lib.tree_conv_backward(x.data_ptr(), w.data_ptr(), p(bias), dy.data_ptr(), p(init_ctx), dx.data_ptr(),
+                                  dw.data_ptr(), p(db), p(dctx), n, c, _dtype_code(x), a, plan.handle,
+                                  dplan.data_ptr(), workspace.data_ptr(), workspace.numel(), stream))
+    return dx, dw, db, dctx
 
 
 def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_states: bool = False,

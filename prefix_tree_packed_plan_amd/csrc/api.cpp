@@ -35,6 +35,12 @@ int hip_fail(const char* what, hipError_t e) {
 
 bool dtype_ok(int32_t d) { return d == TREE_DTYPE_F32 || d == TREE_DTYPE_BF16; }
 
+// Blocks along the tokens of the conv backward (each walks every n-th tile).
+int32_t conv_bwd_parts(const tg::Plan& p) {
+  const int64_t tiles = (p.n_tokens + 63) / 64;
+  return static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(tiles, 512)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,6 +148,67 @@ int tree_conv(const void* x, const void* w, const void* bias, void* y, const voi
                  base + p.m_seg_off, base + p.m_hist, p.n_seg, init_ctx, ctx_out, base + p.m_ctx};
   const hipError_t e = tg::launch_conv(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("tree_conv: launch", e);
+  return TREE_OK;
+}
+
+size_t tree_conv_backward_workspace_bytes(const tree_plan_t* plan, int32_t channels) {
+  if (!plan || channels <= 0) return 0;
+  const tg::Plan& p = plan->p;
+  const size_t heads = static_cast<size_t>(p.n_seg) * std::max(p.width - 1, 0) * channels;
+  const size_t part = static_cast<size_t>(conv_bwd_parts(p)) * channels * (p.width + 1);
+  return (heads + part) * sizeof(float);
+}
+
+int tree_conv_backward(const void* x, const void* w, const void* bias, const void* dy, const void* init_ctx,
+                       void* dx, float* dw, float* dbias, float* dinit_ctx, int64_t n_tokens, int32_t channels,
+                       int32_t dtype, int32_t act, const tree_plan_t* plan, const void* dplan, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!plan || !x || !w || !dy || !dx || !dw || !dplan)
+    return fail(TREE_ERR_INVALID_ARG, "tree_conv_backward: null argument");
+  const tg::Plan& p = plan->p;
+  if (n_tokens != p.n_tokens)
+    return fail(TREE_ERR_SIZE, "tree_conv_backward: n_tokens %lld != plan tokens %lld",
+                static_cast<long long>(n_tokens), static_cast<long long>(p.n_tokens));
+  if (channels <= 0) return fail(TREE_ERR_INVALID_ARG, "tree_conv_backward: channels must be > 0");
+  if (!dtype_ok(dtype)) return fail(TREE_ERR_INVALID_ARG, "tree_conv_backward: bad dtype %d", dtype);
+  if (act != TREE_ACT_NONE && act != TREE_ACT_SILU)
+    return fail(TREE_ERR_INVALID_ARG, "tree_conv_backward: bad activation %d", act);
+  if (p.width > 4) return fail(TREE_ERR_UNSUPPORTED, "tree_conv_backward: conv width %d > 4", p.width);
+  if (dx == x || dx == dy) return fail(TREE_ERR_INVALID_ARG, "tree_conv_backward: dx must not alias x or dy");
+  const size_t need = tree_conv_backward_workspace_bytes(plan, channels);
+  if (!ws || ws_bytes < need)
+    return fail(TREE_ERR_WORKSPACE, "tree_conv_backward: workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0,
+                need);
+  const int32_t* base = static_cast<const int32_t*>(dplan);
+  tg::ConvBwdArgs a{};
+  a.x = x;
+  a.w = w;
+  a.bias = bias;
+  a.dy = dy;
+  a.init_ctx = init_ctx;
+  a.dx = dx;
+  a.dw = dw;
+  a.dbias = bias ? dbias : nullptr;
+  a.dinit_ctx = p.width > 1 ? dinit_ctx : nullptr;
+  a.heads = static_cast<float*>(ws);
+  a.part = a.heads + static_cast<size_t>(p.n_seg) * std::max(p.width - 1, 0) * channels;
+  a.n_part = conv_bwd_parts(p);
+  a.n_tok = static_cast<int32_t>(n_tokens);
+  a.channels = channels;
+  a.width = p.width;
+  a.dtype = dtype;
+  a.act = act;
+  a.n_seg = p.n_seg;
+  a.n_roots = p.n_roots;
+  a.seg_off = base + p.m_seg_off;
+  a.hist = base + p.m_hist;
+  a.fut_off = base + p.m_fut_off;
+  a.fut = base + p.m_fut;
+  a.ent_off = base + p.m_ent_off;
+  a.ent = base + p.m_ent;
+  a.roots = base + p.m_roots;
+  const hipError_t e = tg::launch_conv_backward(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("tree_conv_backward: launch", e);
   return TREE_OK;
 }
 

@@ -28,6 +28,37 @@ struct ConvArgs {
 // Returns hipSuccess or the launch error.
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 
+struct ConvBwdArgs {
+  const void* x;
+  const void* w;
+  const void* bias;      // may be null
+  const void* dy;
+  const void* init_ctx;  // may be null
+  void* dx;
+  float* dw;             // [C, W]
+  float* dbias;          // [C] or null
+  float* dinit_ctx;      // [n_roots, W-1, C] or null
+  float* heads;          // workspace [n_seg (W-1), C]: dz of each segment's first W-1 tokens
+  float* part;           // workspace [n_part, C, W + 1]: per-block dw, dbias partials
+  int32_t n_part;
+  int32_t n_tok;
+  int32_t channels;
+  int32_t width;
+  int32_t dtype;
+  int32_t act;
+  int32_t n_seg;
+  int32_t n_roots;
+  const int32_t* seg_off;
+  const int32_t* hist;
+  const int32_t* fut_off;  // [n_seg (W-1) + 1]
+  const int32_t* fut;      // head rows m steps past a segment's end
+  const int32_t* ent_off;  // [n_seg (W-1) + 1]
+  const int32_t* ent;      // head rows m steps after a segment's start
+  const int32_t* roots;    // [n_roots], segment order
+};
+
+hipError_t launch_conv_backward(const ConvBwdArgs& a, hipStream_t stream);
+
 struct ScanArgs {
   const void* q;
   const void* k;

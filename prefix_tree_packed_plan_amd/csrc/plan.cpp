@@ -169,6 +169,42 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
     }
   }
 
+  // Conv backward head tables: ent bottom-up (children have larger indices).
+  {
+    std::vector<std::vector<int32_t>> kids(n_seg);
+    for (int32_t i = 0; i < n_seg; ++i)
+      if (p.parents[i] >= 0) kids[p.parents[i]].push_back(i);
+      else p.roots.push_back(i);
+    std::vector<std::vector<int32_t>> ent(static_cast<size_t>(n_seg) * std::max(H, 1));
+    for (int32_t i = n_seg - 1; i >= 0 && H > 0; --i) {
+      for (int32_t m = 0; m < H; ++m) {
+        auto& e = ent[static_cast<size_t>(i) * H + m];
+        if (m < p.lens[i]) {
+          e.push_back(i * H + m);
+        } else {
+          for (const int32_t c : kids[i]) {
+            const auto& ce = ent[static_cast<size_t>(c) * H + (m - p.lens[i])];
+            e.insert(e.end(), ce.begin(), ce.end());
+          }
+        }
+      }
+    }
+    p.ent_off.assign(1, 0);
+    p.fut_off.assign(1, 0);
+    for (int32_t i = 0; i < n_seg && H > 0; ++i) {
+      for (int32_t m = 0; m < H; ++m) {
+        const auto& e = ent[static_cast<size_t>(i) * H + m];
+        p.ent.insert(p.ent.end(), e.begin(), e.end());
+        p.ent_off.push_back(static_cast<int32_t>(p.ent.size()));
+        for (const int32_t c : kids[i]) {
+          const auto& ce = ent[static_cast<size_t>(c) * H + m];
+          p.fut.insert(p.fut.end(), ce.begin(), ce.end());
+        }
+        p.fut_off.push_back(static_cast<int32_t>(p.fut.size()));
+      }
+    }
+  }
+
   // Device mirror.
   p.m_seg_off = 0;
   p.m_parent = p.m_seg_off + n_seg + 1;
@@ -179,7 +215,12 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   p.m_ctx = p.m_root + n_seg;
   p.m_path_off = p.m_ctx + p.ctx_src.size();
   p.m_path_seg = p.m_path_off + p.path_off.size();
-  p.mirror.resize(p.m_path_seg + p.path_seg.size());
+  p.m_ent_off = p.m_path_seg + p.path_seg.size();
+  p.m_ent = p.m_ent_off + p.ent_off.size();
+  p.m_fut_off = p.m_ent + p.ent.size();
+  p.m_fut = p.m_fut_off + p.fut_off.size();
+  p.m_roots = p.m_fut + p.fut.size();
+  p.mirror.resize(p.m_roots + p.roots.size());
   std::copy(p.seg_off.begin(), p.seg_off.end(), p.mirror.begin() + p.m_seg_off);
   std::copy(p.parents.begin(), p.parents.end(), p.mirror.begin() + p.m_parent);
   std::copy(p.slot.begin(), p.slot.end(), p.mirror.begin() + p.m_slot);
@@ -189,6 +230,11 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   std::copy(p.ctx_src.begin(), p.ctx_src.end(), p.mirror.begin() + p.m_ctx);
   std::copy(p.path_off.begin(), p.path_off.end(), p.mirror.begin() + p.m_path_off);
   std::copy(p.path_seg.begin(), p.path_seg.end(), p.mirror.begin() + p.m_path_seg);
+  std::copy(p.ent_off.begin(), p.ent_off.end(), p.mirror.begin() + p.m_ent_off);
+  std::copy(p.ent.begin(), p.ent.end(), p.mirror.begin() + p.m_ent);
+  std::copy(p.fut_off.begin(), p.fut_off.end(), p.mirror.begin() + p.m_fut_off);
+  std::copy(p.fut.begin(), p.fut.end(), p.mirror.begin() + p.m_fut);
+  std::copy(p.roots.begin(), p.roots.end(), p.mirror.begin() + p.m_roots);
 
   *out = std::move(p);
   return TREE_OK;

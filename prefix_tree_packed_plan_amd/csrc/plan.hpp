@@ -47,10 +47,19 @@ struct Plan {
   int64_t path_entries = 0;  // sum over leaves of (depth + 1)
   std::vector<int32_t> path_off, path_seg;
 
+  // Conv backward: "head" rows h = s (W-1) + j name token j < W-1 of segment
+  // s.  ent[s][m] (CSR over s (W-1) + m) lists the head rows of the tokens
+  // m steps after segment s's first token along any path (s's own token m
+  // if it has one, else the children's, recursively); fut[s][m] those m
+  // steps after s's last token, i.e. the union of the children's ent[c][m].
+  // roots: the roots in segment order.
+  std::vector<int32_t> ent_off, ent, fut_off, fut, roots;
+
   // Device copy: one int32 array; element offsets of each table inside it.
   std::vector<int32_t> mirror;
   size_t m_seg_off = 0, m_parent = 0, m_slot = 0, m_hist = 0, m_order = 0, m_root = 0, m_ctx = 0;
   size_t m_path_off = 0, m_path_seg = 0;
+  size_t m_ent_off = 0, m_ent = 0, m_fut_off = 0, m_fut = 0, m_roots = 0;
 
   size_t device_bytes() const { return mirror.size() * sizeof(int32_t); }
 };
