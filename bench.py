@@ -120,6 +120,7 @@ def main():
                     help="scan schedule of the timed step (auto = the fork/rescan policy)")
     ap.add_argument("--no-rescan-compare", action="store_true",
                     help="skip the untimed-by-the-step comparison run of the rescan schedule")
+    ap.add_argument("--no-backward", action="store_true", help="skip the separately timed conv backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="before timing, run one plain 1 GiB device copy (a counter reference for profiles)")
@@ -195,6 +196,30 @@ def main():
         torch.cuda.synchronize()
         other = {"schedule": alt, "scan_ms": ev[0].elapsed_time(ev[1]) / reps, "reps": reps}
 
+    # The conv backward on the same trie (timed on its own, outside the step):
+    # dy of the conv output -> dx, dw, dbias.
+    bwd = None
+    if not args.no_backward:
+        dy = torch.empty_like(t["x"]).normal_()
+        bias0 = torch.zeros(s.channels, dtype=t["x"].dtype, device=dev)
+        dx = torch.empty_like(t["x"])
+        bws = torch.empty(max(int(lib.tree_conv_backward_workspace_bytes(plan.handle, s.channels)), 1),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            ptp.tree_conv_backward(t["x"], t["w"], dy, plan, bias=bias0, dx=dx, workspace=bws)
+        reps = max(3, min(args.steps, 10))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            ptp.tree_conv_backward(t["x"], t["w"], dy, plan, bias=bias0, dx=dx, workspace=bws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        bms = ev[0].elapsed_time(ev[1]) / reps
+        bb = 3 * wl.n_tokens * conv_bytes_per_token(s) // 2  # read x and dy, write dx
+        bwd = {"tree_conv_backward": {"ms": bms, "bytes": bb, "GB/s": bb / bms / 1e6,
+                                      "roofline_frac": bb / (HBM_PEAK_GBS * 1e9) / (bms * 1e-3), "reps": reps}}
+        del dy, dx, bws
+
     n = wl.n_tokens
     state_bytes = 2 * st["n_parents"] * s.h_v * s.d_k * s.d_v * 4  # write + read once
     conv_b = n * conv_bytes_per_token(s)
@@ -246,6 +271,8 @@ def main():
         "kernels": kernels,
         "roofline_combined_frac": ((conv_b + scan_b) / (HBM_PEAK_GBS * 1e9)) / ((conv_ms + scan_ms) * 1e-3),
     }
+    if bwd is not None:
+        out["backward"] = bwd
     if other is not None:
         fork_ms = scan_ms if sched == "level" else other["scan_ms"]
         rescan_ms = other["scan_ms"] if sched == "level" else scan_ms

@@ -366,9 +366,27 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_main_kernel(
     }
     float ring[W][VEC];  // ring[k] = dz of the token k steps before the current one
     const int32_t t_stop = min(t1 + H, n_tok);
-    for (int32_t t = t0; t < t_stop; ++t) {
+    bool done = false;
+    for (int32_t tb = t0; tb < t_stop && !done; tb += kBatch) {
+    // x and dy of kBatch tokens in flight together (rows past a segment
+    // break in the lookahead are loaded and not used; all are < n_tok).
+    float xb[kBatch][VEC], db[kBatch][VEC];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (tb + u < t_stop) {
+        load_row<T, VEC>(x + static_cast<int64_t>(tb + u) * C + c0, xb[u]);
+        load_row<T, VEC>(dy + static_cast<int64_t>(tb + u) * C + c0, db[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int32_t t = tb + u;
+      if (t >= t_stop) break;
       if (t == seg_end) {  // next segment
-        if (t >= t1) break;  // the lookahead stays in the tile's last segment
+        if (t >= t1) {  // the lookahead stays in the tile's last segment
+          done = true;
+          break;
+        }
         ++s;
         seg_start = seg_end;
         seg_end = seg_off[s + 1];
@@ -376,15 +394,14 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_main_kernel(
         for (int j = 0; j < H; ++j)
           load_hist<T, VEC>(x, ctx, hist[static_cast<int64_t>(s) * H + H - 1 - j], C, c0, win[j]);
       }
-      float xv[VEC], dv[VEC], dz[VEC];
-      load_row<T, VEC>(x + static_cast<int64_t>(t) * C + c0, xv);
-      load_row<T, VEC>(dy + static_cast<int64_t>(t) * C + c0, dv);
+      const float(&xv)[VEC] = xb[u];
+      float dz[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         float z = br[e] + wr[W - 1][e] * xv[e];
 #pragma unroll
         for (int j = 0; j < H; ++j) z += wr[W - 2 - j][e] * win[j][e];
-        dz[e] = dact(z, dv[e], act);
+        dz[e] = dact(z, db[u][e], act);
       }
       if (t < t1) {
 #pragma unroll
@@ -449,6 +466,7 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_main_kernel(
 #pragma unroll
         for (int e = 0; e < VEC; ++e) win[0][e] = xv[e];
       }
+    }
     }
   }
   float* pp = part + (static_cast<int64_t>(blockIdx.y) * C + c0) * (W + 1);
