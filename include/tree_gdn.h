@@ -1,5 +1,5 @@
 /*
- * tree_gdn.h -- C ABI of the tree conv + tree Gated DeltaNet forward library
+ * tree_gdn.h -- C ABI of the tree conv + tree Gated DeltaNet library (forward and backward)
  * for AMD Instinct MI355X (gfx950).
  *
  * The library runs the forward pass of a recurrent mixer over a prefix trie
@@ -301,6 +301,51 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g,
                   int32_t h_v, int32_t d_k, int32_t d_v, float scale, int32_t dtype,
                   int32_t sched, const tree_plan_t* plan, const void* dplan, void* ws,
                   size_t ws_bytes, void* stream);
+
+/*
+ * tree_gdn_scan_backward_workspace_bytes -- device workspace
+ * tree_gdn_scan_backward needs: the start state of every 16-token chunk of
+ * the largest trie level and one start-state gradient per segment,
+ * [h_v, d_k, d_v] fp32 each, plus per-value-head dq and dk
+ * ([n_tokens, h_v, d_k] fp32 each) when h_v != h_qk.
+ */
+size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h_qk, int32_t h_v, int32_t d_k,
+                                              int32_t d_v);
+
+/*
+ * tree_gdn_scan_backward -- gradients of tree_gdn_scan ("Tree Training"
+ * section 3.1 Eq. 6, every token's output counted once; section 3.2 Eq. 10
+ * and appendix A.2, each segment starting from its parent's final state).
+ * Given do = dL/do (and optionally dstates = dL/dstates), returns dL/dq,
+ * dL/dk, dL/dv, dL/dg, dL/dbeta and dL/dinit_states.  A parent's final
+ * state receives the sum of the gradients of all its children's start
+ * states, in fp32 and in child index order (appendix A.2, sibling
+ * gradients accumulate in the shared parent state; appendix B.5, fp32
+ * accumulation); levels run from the deepest up.  The result is
+ * deterministic.  Within a segment the chunked form is differentiated
+ * chunk by chunk (16-token chunks, fp32 MFMA), each chunk's start state
+ * recomputed from the parent's final state.
+ * q, k, v, g, beta, init_states, scale, dtype   as passed to tree_gdn_scan.
+ * dout    device, [n_tokens, h_v, d_v], dtype        (read)
+ * dstates device, [n_seg, h_v, d_k, d_v] fp32, or NULL (no gradient on the
+ *         final states)                               (read)
+ * states  device, [n_seg, h_v, d_k, d_v] fp32: the final states the
+ *         forward wrote (tree_gdn_scan's `states`)    (read)
+ * dq, dk  device, [n_tokens, h_qk, d_k] fp32 (summed over the value heads
+ *         of each query/key head, in head order)      (written)
+ * dv      device, [n_tokens, h_v, d_v] fp32           (written)
+ * dg, dbeta device, [n_tokens, h_v] fp32              (written)
+ * dinit_states device, [n_roots, h_v, d_k, d_v] fp32, or NULL (written)
+ * ws      device workspace of ws_bytes >= tree_gdn_scan_backward_workspace_bytes.
+ * Compiled head sizes: d_k = d_v in {32, 64, 128}; bf16 or fp32 inputs.
+ * Errors: INVALID_ARG, SIZE, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const void* dout, const float* dstates, const float* init_states,
+                           const float* states, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                           float* dinit_states, int64_t n_tokens, int32_t h_qk, int32_t h_v, int32_t d_k,
+                           int32_t d_v, float scale, int32_t dtype, const tree_plan_t* plan, const void* dplan,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* Message for the last failed call on this thread ("" if none). */
 const char* tree_last_error(void);

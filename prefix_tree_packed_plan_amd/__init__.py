@@ -14,5 +14,6 @@ from ._lib import (  # noqa: F401
     tree_conv,
     tree_conv_backward,
     tree_gdn_scan,
+    tree_gdn_scan_backward,
     tree_plan,
 )

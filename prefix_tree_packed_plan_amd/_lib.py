@@ -68,6 +68,9 @@ SIGNATURES = {
     "tree_scan_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
     "tree_gdn_scan": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
                                      _F, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "tree_gdn_scan_backward_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
+    "tree_gdn_scan_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
+                                              _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _SZ, _P]),
     "tree_last_error": (ctypes.c_char_p, []),
 }
 
@@ -362,3 +365,61 @@ def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_s
     if return_states:
         return o, states
     return o
+
+
+def tree_gdn_scan_backward(q, k, v, g, beta, do, plan: TreePlan, states, scale: float = 1.0,
+                           init_states=None, dstates=None, workspace=None):
+    """Gradients of the tree gated delta rule, given the upstream gradient do
+    [N, H_v, d_v] of the outputs (and optionally dstates [n_seg, H_v, d_k,
+    d_v] of every segment's final state) and the forward's final states
+    `states` [n_seg, H_v, d_k, d_v] fp32 (tree_gdn_scan(..., return_states=True)).
+
+    Returns fp32 (dq [N, H_qk, d_k], dk [N, H_qk, d_k], dv [N, H_v, d_v],
+    dg [N, H_v], dbeta [N, H_v], dinit_states [n_roots, H_v, d_k, d_v])."""
+    import torch
+    _need(q, "q")
+    dev = q.device
+    f32 = torch.float32
+    _need(k, "k", q.dtype, dev)
+    _need(v, "v", q.dtype, dev)
+    _need(do, "do", q.dtype, dev)
+    _need(g, "g", f32, dev)
+    _need(beta, "beta", f32, dev)
+    _need(states, "states", f32, dev)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0] or do.shape != v.shape:
+        raise ValueError("shapes must be q, k [N, H_qk, d_k] and v, do [N, H_v, d_v]")
+    n, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    if g.shape != (n, h_v) or beta.shape != (n, h_v):
+        raise ValueError("g and beta must be [N, H_v]")
+    st_shape = (plan.n_seg, h_v, d_k, d_v)
+    if tuple(states.shape) != st_shape:
+        raise ValueError("states must be [n_seg, H_v, d_k, d_v]")
+    if dstates is not None:
+        _need(dstates, "dstates", f32, dev)
+        if tuple(dstates.shape) != st_shape:
+            raise ValueError("dstates must be [n_seg, H_v, d_k, d_v]")
+    if init_states is not None:
+        _need(init_states, "init_states", f32, dev)
+        if tuple(init_states.shape) != (plan.n_roots, h_v, d_k, d_v):
+            raise ValueError("init_states must be [n_roots, H_v, d_k, d_v]")
+    dq = torch.empty((n, h_qk, d_k), dtype=f32, device=dev)
+    dk = torch.empty((n, h_qk, d_k), dtype=f32, device=dev)
+    dv = torch.empty((n, h_v, d_v), dtype=f32, device=dev)
+    dg = torch.empty((n, h_v), dtype=f32, device=dev)
+    db = torch.empty((n, h_v), dtype=f32, device=dev)
+    dinit = torch.empty((plan.n_roots, h_v, d_k, d_v), dtype=f32, device=dev)
+    lib = load()
+    need = int(lib.tree_gdn_scan_backward_workspace_bytes(plan.handle, h_qk, h_v, d_k, d_v))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    dplan = plan.on_device(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    _check(lib.tree_gdn_scan_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                                      do.data_ptr(), p(dstates), p(init_states), states.data_ptr(),
+                                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), db.data_ptr(),
+                                      dinit.data_ptr(), n, h_qk, h_v, d_k, d_v, float(scale), _dtype_code(q),
+                                      plan.handle, dplan.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      stream))
+    return dq, dk, dv, dg, db, dinit

@@ -283,6 +283,89 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, c
   return TREE_OK;
 }
 
+size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h_qk, int32_t h_v, int32_t d_k,
+                                              int32_t d_v) {
+  if (!plan || h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0) return 0;
+  const tg::Plan& p = plan->p;
+  const size_t dd = static_cast<size_t>(d_k) * d_v;
+  size_t n = (static_cast<size_t>(p.max_level_chunks) + p.n_seg) * h_v * dd;
+  if (h_v != h_qk) n += 2 * static_cast<size_t>(p.n_tokens) * h_v * d_k;
+  return n * sizeof(float);
+}
+
+int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                           const void* dout, const float* dstates, const float* init_states,
+                           const float* states, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                           float* dinit_states, int64_t n_tokens, int32_t h_qk, int32_t h_v, int32_t d_k,
+                           int32_t d_v, float scale, int32_t dtype, const tree_plan_t* plan, const void* dplan,
+                           void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !q || !k || !v || !g || !beta || !dout || !states || !dq || !dk || !dv || !dg || !dbeta || !dplan)
+    return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan_backward: null argument");
+  const tg::Plan& p = plan->p;
+  if (n_tokens != p.n_tokens)
+    return fail(TREE_ERR_SIZE, "tree_gdn_scan_backward: n_tokens %lld != plan tokens %lld",
+                static_cast<long long>(n_tokens), static_cast<long long>(p.n_tokens));
+  if (h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0)
+    return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan_backward: head counts and sizes must be > 0");
+  if (h_v % h_qk != 0)
+    return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan_backward: h_v %d is not a multiple of h_qk %d", h_v, h_qk);
+  if (!dtype_ok(dtype)) return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan_backward: bad dtype %d", dtype);
+  if (!tg::scan_backward_supported(d_k, d_v, dtype))
+    return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan_backward: d_k=%d d_v=%d dtype=%d not compiled in", d_k, d_v,
+                dtype);
+  const size_t need = tree_gdn_scan_backward_workspace_bytes(plan, h_qk, h_v, d_k, d_v);
+  if (!ws || ws_bytes < need)
+    return fail(TREE_ERR_WORKSPACE, "tree_gdn_scan_backward: workspace has %zu bytes, needs %zu",
+                ws ? ws_bytes : 0, need);
+  const int32_t* base = static_cast<const int32_t*>(dplan);
+  const size_t dd = static_cast<size_t>(d_k) * d_v;
+  tg::ScanBwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.dout = dout;
+  a.dstates = dstates;
+  a.init = init_states;
+  a.states = states;
+  a.dv = dv;
+  a.dg = dg;
+  a.dbeta = dbeta;
+  a.dinit = dinit_states;
+  a.hws = static_cast<float*>(ws);
+  a.dsseg = a.hws + static_cast<size_t>(p.max_level_chunks) * h_v * dd;
+  float* per_head = a.dsseg + static_cast<size_t>(p.n_seg) * h_v * dd;
+  const bool grouped = h_v != h_qk;
+  a.dq = grouped ? per_head : dq;
+  a.dk = grouped ? per_head + static_cast<size_t>(n_tokens) * h_v * d_k : dk;
+  a.dq_heads = grouped ? h_v : h_qk;
+  a.seg_off = base + p.m_seg_off;
+  a.parent = base + p.m_parent;
+  a.root_idx = base + p.m_root;
+  a.kid_off = base + p.m_kid_off;
+  a.kid = base + p.m_kid;
+  a.bchunk = base + p.m_bchunk;
+  a.h_qk = h_qk;
+  a.h_v = h_v;
+  a.scale = scale;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // Deepest level first: a parent sums its children's start-state gradients.
+  for (int32_t l = p.n_levels - 1; l >= 0; --l) {
+    a.items = base + p.m_order + p.level_start[l];
+    a.n_items = p.level_start[l + 1] - p.level_start[l];
+    const hipError_t e = tg::launch_scan_backward_level(a, d_k, dtype, st);
+    if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);
+  }
+  if (grouped) {
+    const int group = h_v / h_qk;
+    hipError_t e = tg::launch_head_group_sum(a.dq, dq, n_tokens, h_qk, group, d_k, st);
+    if (e == hipSuccess) e = tg::launch_head_group_sum(a.dk, dk, n_tokens, h_qk, group, d_k, st);
+    if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);
+  }
+  return TREE_OK;
+}
+
 const char* tree_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

@@ -1,0 +1,595 @@
+// Backward of the chunked tree Gated DeltaNet for gfx950 (CDNA4).
+//
+// Method: "Tree Training" (arXiv 2511.00413) section 3.1 Eq. 6 (every
+// token's output counted once), section 3.2 "SSM Layers (GDN)" Eq. 10 and
+// appendix A.2: a segment starts from its parent's final state, so the
+// gradient of that state is the sum over all children of the gradients of
+// their start states, accumulated in fp32 (appendix B.5).  Segments run
+// level by level from the deepest up; within a segment, 16-token chunks run
+// from the last to the first.
+//
+// Chunk algebra (start state S0 [d_k, d_v], G the within-chunk cumulative
+// sum of g, gamma = exp(G), delta_i = exp(G_last - G_i),
+// Gamma_ij = exp(G_i - G_j) for j <= i):
+//   forward   KK = K K^T, A = tril(diag(b) (KK o Gamma), -1), T = (I + A)^-1,
+//             W0 = V - diag(gamma) K S0, R = diag(b) W0, U = T R,
+//             P = tril(Q K^T o Gamma), O = scale (diag(gamma) Q S0 + P U),
+//             S1 = gamma_last S0 + K^T diag(delta) U;
+//   backward  (dOs = scale dO, dS1 the gradient of S1)
+//             dU  = diag(delta) K dS1 + P^T dOs,  dR = T^T dU,
+//             dA  = -tril(dR U^T, -1),            dP = tril(dOs U^T),
+//             dV  = diag(b) dR,
+//             dQ  = diag(gamma) dOs S0^T + (dP o Gamma) K,
+//             dK  = diag(delta) U dS1^T - diag(gamma) dV S0^T + (dP o Gamma)^T Q
+//                   + (dKK + dKK^T) K,  dKK = diag(b) (dA o Gamma),
+//             db  = rowsum(dR o W0) + rowsum(dA o KK o Gamma),
+//             dS0 = gamma_last dS1 + Q^T diag(gamma) dOs - K^T diag(gamma) dV,
+//   and the gate gradient through G: with dGam = dP o QK + diag(b) (dA o KK)
+//   and M = dGam o Gamma,
+//             dG_i = gamma_i rowsum(Q S0 o dOs - dV o K S0)_i
+//                    - delta_i rowsum(K dS1 o U)_i + rowsum(M)_i - colsum(M)_i,
+//             dG_last += gamma_last sum(S0 o dS1) + sum_i delta_i rowsum(K dS1 o U)_i,
+//             dg_t = sum_{i >= t} dG_i within the chunk.
+// (dT = dU R^T and dA = -T^T dT T^T reduce to -dR U^T because T R = U.)
+// (I + A)^-1 for the nilpotent A is the product
+// (I + N)(I + N^2)(I + N^4)(I + N^8), N = -A: six 16x16 MFMA products.
+//
+// Work item: one segment and one value head per work-group of d/16 waves.
+// Pass 1 re-runs the segment's chunks forward from the parent's final state
+// (the forward's `states`) and writes every chunk's start state to the
+// workspace; pass 2 walks the chunks backwards.  Wave w owns column tile w
+// (16 columns) of every [16, d] chunk tensor and of the state gradient dS,
+// which stays in MFMA accumulator registers across the segment.
+//
+// MFMA: v_mfma_f32_16x16x4_f32 (fp32 inputs, fp32 accumulate) throughout.
+// Lane l = 16 h + i (h = l / 16) holds accumulator rows 4h + r, column i.
+// A 16-deep contraction is four MFMAs; in step s lane l supplies index
+// 4h + s of the contraction, so an accumulator tile is the B operand of a
+// product that contracts its rows, and the accumulator tile of X^T is the A
+// operand of a product with X on the left.
+#include <hip/hip_runtime.h>
+
+#include "../../include/tree_gdn.h"
+#include "launch.hpp"
+
+namespace tg {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int L = 16;  // chunk length (tokens)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// c + A B over a 16-deep contraction: a[s] = A[i][4h + s], b[s] = B[4h + s][i].
+__device__ __forceinline__ f32x4 mm(const f32x4 a, const f32x4 b, f32x4 c) {
+  c = mfma(a[0], b[0], c);
+  c = mfma(a[1], b[1], c);
+  c = mfma(a[2], b[2], c);
+  return mfma(a[3], b[3], c);
+}
+__device__ __forceinline__ f32x4 z4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of a row (lanes 16h .. 16h+15); every lane gets it.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
+template <int D>
+struct BwdSmem {
+  static constexpr int S = D + 4;  // row stride (floats) of the [16, d] and [d, d] tables
+  static constexpr int NW = D / 16;
+  // Small tables first and dS1 last: every address below stays within the
+  // 64 KiB reach of an LDS instruction's offset from one base register.
+  alignas(16) float g[L];
+  alignas(16) float b[L];
+  alignas(16) float gl[NW][4];          // per-wave partial sum(S0 o dS1)
+  alignas(16) float rows[NW][3][L];     // per-wave partial row sums
+  alignas(16) float m[2][L * 17];       // M and dA o KK o Gamma
+  alignas(16) float part[NW][2][L * L];  // per-wave 16x16 partial products
+  alignas(16) float q[L * S];
+  alignas(16) float k[L * S];
+  alignas(16) float o[L * S];  // scale * dO
+  alignas(16) float u[L * S];
+  alignas(16) float r[L * S];  // dR
+  alignas(16) float ds[D * S];  // dS1
+};
+
+// Per-lane gate values of one chunk.
+struct Gates {
+  f32x4 gam, del, bet;  // gamma, delta, beta at rows 4h + r
+  f32x4 Gm, Gmt;        // Gamma at (row, col) and at (col, row), zero where masked
+  float gam_c, del_c, bet_c, gam_last;  // at column i, and gamma_last
+};
+
+__device__ __forceinline__ Gates make_gates(const float* g, const float* b, int h4, int i16) {
+  float grow[4] = {0.f, 0.f, 0.f, 0.f}, gcol = 0.f, run = 0.f;
+#pragma unroll
+  for (int t = 0; t < L; ++t) {
+    run += g[t];  // the same running sum in every lane: G is bitwise consistent
+#pragma unroll
+    for (int r = 0; r < 4; ++r) grow[r] = (t == 4 * h4 + r) ? run : grow[r];
+    gcol = (t == i16) ? run : gcol;
+  }
+  const float glast = run * kLog2e, gc = gcol * kLog2e;
+  Gates s;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * h4 + r;
+    const float gr = grow[r] * kLog2e;
+    s.gam[r] = ex2(gr);
+    s.del[r] = ex2(glast - gr);
+    s.bet[r] = b[row];
+    s.Gm[r] = row >= i16 ? ex2(gr - gc) : 0.f;
+    s.Gmt[r] = i16 >= row ? ex2(gc - gr) : 0.f;
+  }
+  s.gam_c = ex2(gc);
+  s.del_c = ex2(glast - gc);
+  s.bet_c = b[i16];
+  s.gam_last = ex2(glast);
+  return s;
+}
+
+// T = (I + A)^-1 and T^T as accumulator tiles from the lane's KK tile.
+// A[row][col] = b_row Gamma[row][col] KK[row][col] for row > col.
+__device__ __forceinline__ void solve(const f32x4 kk, const Gates& s, int h4, int i16, f32x4& T, f32x4& Tt) {
+  f32x4 N, Nt, I;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * h4 + r;
+    N[r] = row > i16 ? -s.bet[r] * s.Gm[r] * kk[r] : 0.f;
+    Nt[r] = i16 > row ? -s.bet_c * s.Gmt[r] * kk[r] : 0.f;  // N[col][row]; KK is symmetric
+    I[r] = row == i16 ? 1.f : 0.f;
+  }
+  // Every factor is a polynomial in N, so all of them commute; X Y takes
+  // X^T's tile as the A operand, (X Y)^T = Y^T X^T takes Y's tile.
+  const f32x4 N2 = mm(Nt, N, z4()), N2t = mm(N, Nt, z4());
+  const f32x4 N4 = mm(N2t, N2, z4()), N4t = mm(N2, N2t, z4());
+  const f32x4 N8 = mm(N4t, N4, z4());
+  const f32x4 X1 = I + N, X1t = I + Nt;
+  const f32x4 X2 = mm(X1t, N2, X1), X2t = mm(N2, X1t, X1t);
+  const f32x4 X3 = mm(X2t, N4, X2), X3t = mm(N4, X2t, X2t);
+  T = mm(X3t, N8, X3);
+  Tt = mm(N8, X3t, X3t);  // (X3 N8)^T = N8^T X3^T; N8^T's A operand is N8's tile
+}
+
+template <bool F32IN>
+__device__ __forceinline__ f32x4 load4(const void* base, size_t idx) {
+  if (F32IN) return ld4(static_cast<const float*>(base) + idx);
+  const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xffff0000u)};
+}
+template <bool F32IN>
+__device__ __forceinline__ float load1(const void* base, size_t idx) {
+  if (F32IN) return static_cast<const float*>(base)[idx];
+  return __uint_as_float(uint32_t(static_cast<const uint16_t*>(base)[idx]) << 16);
+}
+
+template <int D, bool F32IN>
+__global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
+  constexpr int NT = D / 16;  // row tiles of the state = waves
+  constexpr int S = D + 4;
+  using SM = BwdSmem<D>;
+  __shared__ SM sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h4 = lane >> 4;
+  const int i16 = lane & 15;
+  const int col = 16 * w + i16;
+
+  const int item = blockIdx.x / a.h_v;
+  const int h = blockIdx.x - item * a.h_v;
+  const int seg = a.items[item];
+  const int hq = h / (a.h_v / a.h_qk);
+  const int t_beg = a.seg_off[seg], t_end = a.seg_off[seg + 1];
+  const int nc = (t_end - t_beg + L - 1) / L;
+  const size_t DD = size_t(D) * D;
+  const size_t cstride = size_t(a.h_v) * DD;  // between consecutive chunks in the workspace
+  float* hws = a.hws + (size_t(a.bchunk[seg]) * a.h_v + h) * DD;
+  const int dq_head = a.dq_heads == a.h_v ? h : hq;
+
+  // Staging: thread -> (row, 4 columns) of a [16, d] chunk tensor.
+  const int st_row = tid / (D / 4);
+  const int st_col = 4 * (tid % (D / 4));
+
+  auto load_tile = [&](const float* p, f32x4 (&x)[NT]) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[rt][r] = p[size_t(16 * rt + 4 * h4 + r) * D + col];
+  };
+  auto store_tile = [&](float* p, const f32x4 (&x)[NT]) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[size_t(16 * rt + 4 * h4 + r) * D + col] = x[rt][r];
+  };
+
+  // ---- pass 1: chunk start states --------------------------------------------
+  {
+    f32x4 St[NT];
+    const int par = a.parent[seg];
+    const float* src = par >= 0 ? a.states + (size_t(par) * a.h_v + h) * DD
+                                : (a.init ? a.init + (size_t(a.root_idx[seg]) * a.h_v + h) * DD : nullptr);
+    if (src) {
+      load_tile(src, St);
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) St[rt] = z4();
+    }
+    for (int c = 0; c < nc; ++c) {
+      const int t0 = t_beg + c * L;
+      const int n = min(L, t_end - t0);
+      store_tile(hws + c * cstride, St);
+      {
+        const bool in = st_row < n;
+        const f32x4 kv = in ? load4<F32IN>(a.k, (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col) : z4();
+        *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
+        if (tid < L) {
+          const bool tin = tid < n;
+          sm.g[tid] = tin ? a.g[size_t(t0 + tid) * a.h_v + h] : 0.f;
+          sm.b[tid] = tin ? a.beta[size_t(t0 + tid) * a.h_v + h] : 0.f;
+        }
+      }
+      f32x4 vt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * h4 + r;
+        vt[r] = row < n ? load1<F32IN>(a.v, (size_t(t0 + row) * a.h_v + h) * D + col) : 0.f;
+      }
+      __syncthreads();
+      const Gates gt = make_gates(sm.g, sm.b, h4, i16);
+      {
+        const f32x4 ak = ld4(&sm.k[i16 * S + 16 * w + 4 * h4]);
+        const f32x4 kkp = mm(ak, ak, z4());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.part[w][0][(4 * h4 + r) * L + i16] = kkp[r];
+      }
+      f32x4 ks = z4();
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) ks = mm(ld4(&sm.k[i16 * S + 16 * rt + 4 * h4]), St[rt], ks);
+      __syncthreads();
+      f32x4 kk = z4();
+#pragma unroll
+      for (int v = 0; v < NT; ++v)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kk[r] += sm.part[v][0][(4 * h4 + r) * L + i16];
+      f32x4 T, Tt;
+      solve(kk, gt, h4, i16, T, Tt);
+      f32x4 R;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[r] = gt.bet[r] * (vt[r] - gt.gam[r] * ks[r]);
+      const f32x4 U = mm(Tt, R, z4());
+      const f32x4 dU = gt.del * U;
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        f32x4 akt;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) akt[s] = sm.k[(4 * h4 + s) * S + 16 * rt + i16];
+        St[rt] = mm(akt, dU, gt.gam_last * St[rt]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- pass 2: chunks backwards ---------------------------------------------------
+  f32x4 dS[NT];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) dS[rt] = z4();
+  if (a.dstates) load_tile(a.dstates + (size_t(seg) * a.h_v + h) * DD, dS);
+  for (int j = a.kid_off[seg]; j < a.kid_off[seg + 1]; ++j) {
+    f32x4 x[NT];
+    load_tile(a.dsseg + (size_t(a.kid[j]) * a.h_v + h) * DD, x);
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) dS[rt] += x[rt];
+  }
+
+  for (int c = nc - 1; c >= 0; --c) {
+    const int t0 = t_beg + c * L;
+    const int n = min(L, t_end - t0);
+    const float* s0p = hws + c * cstride;
+    f32x4 S0[NT];
+    load_tile(s0p, S0);
+    {
+      const bool in = st_row < n;
+      const size_t qi = (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col;
+      const size_t oi = (size_t(t0 + st_row) * a.h_v + h) * D + st_col;
+      const f32x4 qv = in ? load4<F32IN>(a.q, qi) : z4();
+      const f32x4 kv = in ? load4<F32IN>(a.k, qi) : z4();
+      const f32x4 ov = in ? load4<F32IN>(a.dout, oi) * a.scale : z4();
+      *reinterpret_cast<f32x4*>(&sm.q[st_row * S + st_col]) = qv;
+      *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
+      *reinterpret_cast<f32x4*>(&sm.o[st_row * S + st_col]) = ov;
+      if (tid < L) {
+        const bool tin = tid < n;
+        sm.g[tid] = tin ? a.g[size_t(t0 + tid) * a.h_v + h] : 0.f;
+        sm.b[tid] = tin ? a.beta[size_t(t0 + tid) * a.h_v + h] : 0.f;
+      }
+    }
+    {
+      float* const dsw = &sm.ds[4 * h4 * S + col];
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dsw[(16 * rt + r) * S] = dS[rt][r];
+    }
+    f32x4 vt;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * h4 + r;
+      vt[r] = row < n ? load1<F32IN>(a.v, (size_t(t0 + row) * a.h_v + h) * D + col) : 0.f;
+    }
+    __syncthreads();  // chunk tensors and dS1 staged
+
+    const Gates gt = make_gates(sm.g, sm.b, h4, i16);
+    {
+      const f32x4 ak = ld4(&sm.k[i16 * S + 16 * w + 4 * h4]);
+      const f32x4 aq = ld4(&sm.q[i16 * S + 16 * w + 4 * h4]);
+      const f32x4 kkp = mm(ak, ak, z4());
+      const f32x4 qkp = mm(aq, ak, z4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sm.part[w][0][(4 * h4 + r) * L + i16] = kkp[r];
+        sm.part[w][1][(4 * h4 + r) * L + i16] = qkp[r];
+      }
+    }
+    f32x4 ks = z4(), qs = z4(), kd = z4();  // K S0, Q S0, K dS1 at column tile w
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const f32x4 ak = ld4(&sm.k[i16 * S + 16 * rt + 4 * h4]);
+      const f32x4 aq = ld4(&sm.q[i16 * S + 16 * rt + 4 * h4]);
+      ks = mm(ak, S0[rt], ks);
+      qs = mm(aq, S0[rt], qs);
+      kd = mm(ak, dS[rt], kd);
+    }
+    float glp = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) glp += S0[rt][r] * dS[rt][r];
+    __syncthreads();  // KK, QK partials
+
+    f32x4 kk = z4(), qk = z4();
+#pragma unroll
+    for (int v = 0; v < NT; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kk[r] += sm.part[v][0][(4 * h4 + r) * L + i16];
+        qk[r] += sm.part[v][1][(4 * h4 + r) * L + i16];
+      }
+    f32x4 T, Tt;
+    solve(kk, gt, h4, i16, T, Tt);
+    f32x4 P, W0, R, dOc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * h4 + r;
+      P[r] = row >= i16 ? qk[r] * gt.Gm[r] : 0.f;
+      W0[r] = vt[r] - gt.gam[r] * ks[r];
+      R[r] = gt.bet[r] * W0[r];
+      dOc[r] = sm.o[row * S + col];
+    }
+    const f32x4 U = mm(Tt, R, z4());
+    const f32x4 dU = mm(P, dOc, gt.del * kd);
+    const f32x4 dR = mm(T, dU, z4());
+    const f32x4 dV = gt.bet * dR;
+    f32x4 pg, pd, pb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * h4 + r;
+      if (row < n) a.dv[(size_t(t0 + row) * a.h_v + h) * D + col] = dV[r];
+      pg[r] = row_sum16(qs[r] * dOc[r] - dV[r] * ks[r]);
+      pd[r] = row_sum16(kd[r] * U[r]);
+      pb[r] = row_sum16(dR[r] * W0[r]);
+      sm.u[row * S + col] = U[r];
+      sm.r[row * S + col] = dR[r];
+    }
+    glp = row_sum16(glp);
+    if (i16 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sm.rows[w][0][4 * h4 + r] = pg[r];
+        sm.rows[w][1][4 * h4 + r] = pd[r];
+        sm.rows[w][2][4 * h4 + r] = pb[r];
+      }
+      sm.gl[w][h4] = glp;
+    }
+    __syncthreads();  // U, dR staged
+
+    // S0 rows 16w .. 16w+15 as the B operand of products with S0^T.
+    f32x4 S0row[NT];
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) S0row[jt] = ld4(s0p + size_t(16 * w + i16) * D + 16 * jt + 4 * h4);
+    {
+      const f32x4 au = ld4(&sm.u[i16 * S + 16 * w + 4 * h4]);
+      const f32x4 ar = ld4(&sm.r[i16 * S + 16 * w + 4 * h4]);
+      const f32x4 ao = ld4(&sm.o[i16 * S + 16 * w + 4 * h4]);
+      const f32x4 dap = mm(ar, au, z4());  // dR U^T over this wave's columns
+      const f32x4 dpp_ = mm(ao, au, z4());  // dOs U^T
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sm.part[w][0][(4 * h4 + r) * L + i16] = dap[r];
+        sm.part[w][1][(4 * h4 + r) * L + i16] = dpp_[r];
+      }
+    }
+    __syncthreads();  // dA, dP partials
+
+    f32x4 dA, dAt, dP, dPt;
+    {
+      f32x4 x = z4(), xt = z4(), y = z4(), yt = z4();
+#pragma unroll
+      for (int v = 0; v < NT; ++v)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] += sm.part[v][0][(4 * h4 + r) * L + i16];
+          xt[r] += sm.part[v][0][i16 * L + 4 * h4 + r];
+          y[r] += sm.part[v][1][(4 * h4 + r) * L + i16];
+          yt[r] += sm.part[v][1][i16 * L + 4 * h4 + r];
+        }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * h4 + r;
+        dA[r] = row > i16 ? -x[r] : 0.f;
+        dAt[r] = i16 > row ? -xt[r] : 0.f;
+        dP[r] = row >= i16 ? y[r] : 0.f;
+        dPt[r] = i16 >= row ? yt[r] : 0.f;
+      }
+    }
+    const f32x4 dQKP = dP * gt.Gm, dQKPt = dPt * gt.Gmt;
+    const f32x4 dKK = dA * gt.bet * gt.Gm, dKKt = dAt * gt.bet_c * gt.Gmt;
+    if (w == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * h4 + r;
+        sm.m[0][row * 17 + i16] = (dP[r] * qk[r] + dA[r] * gt.bet[r] * kk[r]) * gt.Gm[r];
+        sm.m[1][row * 17 + i16] = dA[r] * kk[r] * gt.Gm[r];
+      }
+    }
+    f32x4 kc, qc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      kc[r] = sm.k[(4 * h4 + r) * S + col];
+      qc[r] = sm.q[(4 * h4 + r) * S + col];
+    }
+    f32x4 xo = z4(), xv = z4(), xu = z4();  // dOs S0^T, dV S0^T, diag(delta) U dS1^T
+    const float* const dsr = &sm.ds[(16 * w + i16) * S + 4 * h4];
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      const int o4 = i16 * S + 16 * jt + 4 * h4;
+      xo = mm(ld4(&sm.o[o4]), S0row[jt], xo);
+      xv = mm(gt.bet_c * ld4(&sm.r[o4]), S0row[jt], xv);
+      xu = mm(gt.del_c * ld4(&sm.u[o4]), ld4(dsr + 16 * jt), xu);
+    }
+    const f32x4 dQ = gt.gam * xo + mm(dQKPt, kc, z4());
+    f32x4 dK = mm(dQKP, qc, z4());
+    dK = mm(dKKt, kc, dK);
+    dK = mm(dKK, kc, dK);
+    dK = dK + xu - gt.gam * xv;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * h4 + r;
+      if (row < n) {
+        a.dq[(size_t(t0 + row) * a.dq_heads + dq_head) * D + col] = dQ[r];
+        a.dk[(size_t(t0 + row) * a.dq_heads + dq_head) * D + col] = dK[r];
+      }
+    }
+    const f32x4 gdo = gt.gam * dOc, gdv = -(gt.gam * dV);
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      f32x4 aqt, akt;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        aqt[s] = sm.q[(4 * h4 + s) * S + 16 * rt + i16];
+        akt[s] = sm.k[(4 * h4 + s) * S + 16 * rt + i16];
+      }
+      dS[rt] = mm(aqt, gdo, gt.gam_last * dS[rt]);
+      dS[rt] = mm(akt, gdv, dS[rt]);
+    }
+    __syncthreads();  // every read of this chunk's tables done
+
+    if (w == 0 && lane < L) {  // gate gradients of token i = lane
+      const int i = lane;
+      float d_gam = 0.f, d_dl = 0.f, db = 0.f, gl = 0.f, rs = 0.f, cs = 0.f, eb = 0.f;
+#pragma unroll
+      for (int v = 0; v < NT; ++v) {
+        d_gam += sm.rows[v][0][i];
+        d_dl += sm.rows[v][1][i];
+        db += sm.rows[v][2][i];
+        gl += sm.gl[v][0] + sm.gl[v][1] + sm.gl[v][2] + sm.gl[v][3];
+      }
+#pragma unroll
+      for (int j = 0; j < L; ++j) {
+        rs += sm.m[0][i * 17 + j];
+        cs += sm.m[0][j * 17 + i];
+        eb += sm.m[1][i * 17 + j];
+      }
+      const float dl = gt.del_c * d_dl;
+      const float dl_sum = row_sum16(dl);
+      float dG = gt.gam_c * d_gam - dl + rs - cs;
+      if (i == L - 1) dG += gt.gam_last * gl + dl_sum;
+      // dg_t = sum of dG_i over i >= t within the chunk.
+      float dg = 0.f;
+#pragma unroll
+      for (int j = 0; j < L; ++j) {
+        const float x = __shfl(dG, j, 64);
+        dg += j >= i ? x : 0.f;
+      }
+      if (i < n) {
+        a.dg[size_t(t0 + i) * a.h_v + h] = dg;
+        a.dbeta[size_t(t0 + i) * a.h_v + h] = db + eb;
+      }
+    }
+  }
+
+  // Start-state gradient: to the parent (summed there over its children) or
+  // to the root's initial state.
+  const int root = a.root_idx[seg];
+  if (root < 0) {
+    store_tile(a.dsseg + (size_t(seg) * a.h_v + h) * DD, dS);
+  } else if (a.dinit) {
+    store_tile(a.dinit + (size_t(root) * a.h_v + h) * DD, dS);
+  }
+}
+
+// dst[t, j, :] = sum over the G value heads of q/k head j of src[t, j G + m, :],
+// in head order.
+__global__ void head_group_sum(const float* __restrict__ src, float* __restrict__ dst, int64_t n_out4, int G,
+                               int d4) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n_out4) return;
+  const int64_t th = i / d4;  // (token, q/k head)
+  const int c = int(i - th * d4);
+  const f32x4* s = reinterpret_cast<const f32x4*>(src) + (th * G) * d4 + c;
+  f32x4 acc = s[0];
+  for (int m = 1; m < G; ++m) acc += s[int64_t(m) * d4];
+  reinterpret_cast<f32x4*>(dst)[i] = acc;
+}
+
+template <int D, bool F32IN>
+hipError_t launch_bwd_level(const ScanBwdArgs& a, hipStream_t stream) {
+  if (a.n_items <= 0) return hipSuccess;
+  gdn_bwd_kernel<D, F32IN><<<dim3(a.n_items * a.h_v), dim3(4 * D), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool scan_backward_supported(int d_k, int d_v, int dtype) {
+  return d_k == d_v && (d_k == 32 || d_k == 64 || d_k == 128) && (dtype == TREE_DTYPE_BF16 || dtype == TREE_DTYPE_F32);
+}
+
+hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream) {
+  const bool f32 = dtype == TREE_DTYPE_F32;
+  switch (d) {
+    case 32: return f32 ? launch_bwd_level<32, true>(a, stream) : launch_bwd_level<32, false>(a, stream);
+    case 64: return f32 ? launch_bwd_level<64, true>(a, stream) : launch_bwd_level<64, false>(a, stream);
+    case 128: return f32 ? launch_bwd_level<128, true>(a, stream) : launch_bwd_level<128, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_head_group_sum(const float* src, float* dst, int64_t n_tok, int h_qk, int group, int d,
+                                 hipStream_t stream) {
+  const int64_t n4 = n_tok * h_qk * (d / 4);
+  if (n4 == 0) return hipSuccess;
+  const int threads = 256;
+  head_group_sum<<<dim3(unsigned((n4 + threads - 1) / threads)), dim3(threads), 0, stream>>>(src, dst, n4, group,
+                                                                                              d / 4);
+  return hipGetLastError();
+}
+
+}  // namespace tg

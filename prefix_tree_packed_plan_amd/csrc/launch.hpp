@@ -93,4 +93,43 @@ hipError_t launch_scan_d128(const ScanArgs& a, bool paths, hipStream_t stream);
 // Whether (d_k, d_v, dtype) has a compiled scan kernel.
 bool scan_supported(int d_k, int d_v, int dtype);
 
+struct ScanBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  const void* dout;
+  const float* dstates;  // [n_seg, h_v, d, d] or null
+  const float* init;     // [n_roots, h_v, d, d] or null (zeros)
+  const float* states;   // the forward's final states [n_seg, h_v, d, d]
+  float* dq;             // [N, dq_heads, d]
+  float* dk;             // [N, dq_heads, d]
+  float* dv;             // [N, h_v, d]
+  float* dg;             // [N, h_v]
+  float* dbeta;          // [N, h_v]
+  float* dinit;          // [n_roots, h_v, d, d] or null
+  float* hws;            // workspace: chunk start states [max_level_chunks, h_v, d, d]
+  float* dsseg;          // workspace: start-state gradients [n_seg, h_v, d, d]
+  const int32_t* seg_off;
+  const int32_t* parent;
+  const int32_t* root_idx;
+  const int32_t* kid_off;
+  const int32_t* kid;
+  const int32_t* bchunk;
+  const int32_t* items;  // segments of this level
+  int32_t n_items;
+  int32_t h_qk;
+  int32_t h_v;
+  int32_t dq_heads;      // h_qk (dq, dk written per q/k head) or h_v (per value head)
+  float scale;
+};
+
+// Scan backward over one trie level (gdn_backward.hip); d = d_k = d_v.
+hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream);
+// dst[t, j] = sum_m src[t, j group + m] over [n_tok, h_qk * group, d] fp32.
+hipError_t launch_head_group_sum(const float* src, float* dst, int64_t n_tok, int h_qk, int group, int d,
+                                 hipStream_t stream);
+bool scan_backward_supported(int d_k, int d_v, int dtype);
+
 }  // namespace tg

@@ -205,6 +205,28 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
     }
   }
 
+  // Scan backward: children lists and level-local chunk offsets.
+  p.kid_off.assign(n_seg + 1, 0);
+  for (int32_t i = 0; i < n_seg; ++i)
+    if (p.parents[i] >= 0) p.kid_off[p.parents[i] + 1] += 1;
+  for (int32_t i = 0; i < n_seg; ++i) p.kid_off[i + 1] += p.kid_off[i];
+  p.kid.assign(p.kid_off[n_seg], 0);
+  {
+    std::vector<int32_t> fill(p.kid_off.begin(), p.kid_off.end() - 1);
+    for (int32_t i = 0; i < n_seg; ++i)
+      if (p.parents[i] >= 0) p.kid[fill[p.parents[i]]++] = i;
+  }
+  p.bchunk.assign(n_seg, 0);
+  for (int32_t l = 0; l < p.n_levels; ++l) {
+    int64_t c = 0;
+    for (int32_t j = p.level_start[l]; j < p.level_start[l + 1]; ++j) {
+      const int32_t s = p.order[j];
+      p.bchunk[s] = static_cast<int32_t>(c);
+      c += (p.lens[s] + Plan::kBwdChunk - 1) / Plan::kBwdChunk;
+    }
+    p.max_level_chunks = std::max(p.max_level_chunks, c);
+  }
+
   // Device mirror.
   p.m_seg_off = 0;
   p.m_parent = p.m_seg_off + n_seg + 1;
@@ -220,7 +242,10 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   p.m_fut_off = p.m_ent + p.ent.size();
   p.m_fut = p.m_fut_off + p.fut_off.size();
   p.m_roots = p.m_fut + p.fut.size();
-  p.mirror.resize(p.m_roots + p.roots.size());
+  p.m_kid_off = p.m_roots + p.roots.size();
+  p.m_kid = p.m_kid_off + p.kid_off.size();
+  p.m_bchunk = p.m_kid + p.kid.size();
+  p.mirror.resize(p.m_bchunk + p.bchunk.size());
   std::copy(p.seg_off.begin(), p.seg_off.end(), p.mirror.begin() + p.m_seg_off);
   std::copy(p.parents.begin(), p.parents.end(), p.mirror.begin() + p.m_parent);
   std::copy(p.slot.begin(), p.slot.end(), p.mirror.begin() + p.m_slot);
@@ -235,6 +260,9 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   std::copy(p.fut_off.begin(), p.fut_off.end(), p.mirror.begin() + p.m_fut_off);
   std::copy(p.fut.begin(), p.fut.end(), p.mirror.begin() + p.m_fut);
   std::copy(p.roots.begin(), p.roots.end(), p.mirror.begin() + p.m_roots);
+  std::copy(p.kid_off.begin(), p.kid_off.end(), p.mirror.begin() + p.m_kid_off);
+  std::copy(p.kid.begin(), p.kid.end(), p.mirror.begin() + p.m_kid);
+  std::copy(p.bchunk.begin(), p.bchunk.end(), p.mirror.begin() + p.m_bchunk);
 
   *out = std::move(p);
   return TREE_OK;

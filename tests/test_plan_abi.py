@@ -238,3 +238,41 @@ def test_schedule_constants_match_the_header():
     assert val("TREE_SCHED_RESCAN") == _lib.SCHED_RESCAN
     assert val("TREE_SCHED_AUTO") == _lib.SCHED_AUTO
     assert val("TREE_FORK_MIN_SAVED_TOKENS") == _lib.FORK_MIN_SAVED_TOKENS
+
+
+@pytest.mark.parametrize("cid", sorted(CONFIGS))
+def test_scan_backward_workspace_size_and_checks(cid):
+    """Workspace = chunk start states of the level with the most 16-token
+    chunks + one start-state gradient per segment (+ per-value-head dq, dk
+    when value heads share a q/k head), fp32; undersized workspaces and bad
+    arguments are rejected before any device work."""
+    lib = _lib.load()
+    parents, lens, _ = make_trie(cid)
+    s = CONFIGS[cid]
+    plan = _lib.TreePlan(parents, lens, 4)
+    depth = np.zeros(len(parents), np.int64)
+    for i, p in enumerate(parents):
+        depth[i] = depth[p] + 1 if p >= 0 else 0
+    chunks = [int(sum((lens[i] + 15) // 16 for i in range(len(parents)) if depth[i] == lv))
+              for lv in range(int(depth.max()) + 1)]
+    dd = s.d_k * s.d_v
+    want = (max(chunks) + len(parents)) * s.h_v * dd
+    if s.h_v != s.h_qk:
+        want += 2 * int(lens.sum()) * s.h_v * s.d_k
+    need = lib.tree_gdn_scan_backward_workspace_bytes(plan.handle, s.h_qk, s.h_v, s.d_k, s.d_v)
+    assert need == 4 * want
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    bwd = lib.tree_gdn_scan_backward
+    n = plan.n_tokens
+    dt = 0 if s.dtype == "f32" else 1
+
+    def call(n_tok=n, h_qk=s.h_qk, h_v=s.h_v, d=s.d_k, dtype=dt, ws=need, states=fake):
+        return bwd(*([fake] * 6), None, None, states, *([fake] * 5), None, n_tok, h_qk, h_v, d, d, 1.0, dtype,
+                   plan.handle, fake, fake, ws, None)
+
+    assert call(ws=need - 1) == -5
+    assert call(n_tok=n + 1) == -3
+    assert call(d=48) == -4
+    assert call(h_qk=3, h_v=4) == -4
+    assert call(dtype=7) == -1
+    assert call(states=None) == -1
