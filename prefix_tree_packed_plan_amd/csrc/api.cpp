@@ -289,6 +289,7 @@ size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h
   const tg::Plan& p = plan->p;
   const size_t dd = static_cast<size_t>(d_k) * d_v;
   size_t n = (static_cast<size_t>(p.max_level_chunks) + p.n_seg) * h_v * dd;
+  n += static_cast<size_t>(p.max_level_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
   if (h_v != h_qk) n += 2 * static_cast<size_t>(p.n_tokens) * h_v * d_k;
   return n * sizeof(float);
 }
@@ -335,7 +336,8 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.dinit = dinit_states;
   a.hws = static_cast<float*>(ws);
   a.dsseg = a.hws + static_cast<size_t>(p.max_level_chunks) * h_v * dd;
-  float* per_head = a.dsseg + static_cast<size_t>(p.n_seg) * h_v * dd;
+  a.tws = a.dsseg + static_cast<size_t>(p.n_seg) * h_v * dd;
+  float* per_head = a.tws + static_cast<size_t>(p.max_level_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
   const bool grouped = h_v != h_qk;
   a.dq = grouped ? per_head : dq;
   a.dk = grouped ? per_head + static_cast<size_t>(n_tokens) * h_v * d_k : dk;

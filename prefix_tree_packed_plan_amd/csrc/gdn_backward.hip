@@ -201,6 +201,10 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
   const size_t DD = size_t(D) * D;
   const size_t cstride = size_t(a.h_v) * DD;  // between consecutive chunks in the workspace
   float* hws = a.hws + (size_t(a.bchunk[seg]) * a.h_v + h) * DD;
+  // T, KK and QK of every chunk, [16, 16] fp32 each.
+  constexpr int TW = 3 * L * L;
+  const size_t tstride = size_t(a.h_v) * TW;
+  float* tws = a.tws + (size_t(a.bchunk[seg]) * a.h_v + h) * TW;
   const int dq_head = a.dq_heads == a.h_v ? h : hq;
 
   // Staging: thread -> (row, 4 columns) of a [16, d] chunk tensor.
@@ -232,48 +236,78 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) St[rt] = z4();
     }
-    for (int c = 0; c < nc; ++c) {
+    // Inputs of chunk c in registers, fetched one chunk ahead.
+    f32x4 kv, qv, vt;
+    float gv = 0.f, bv = 0.f;
+    auto fetch = [&](int c) {
       const int t0 = t_beg + c * L;
       const int n = min(L, t_end - t0);
-      store_tile(hws + c * cstride, St);
-      {
-        const bool in = st_row < n;
-        const f32x4 kv = in ? load4<F32IN>(a.k, (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col) : z4();
-        *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
-        if (tid < L) {
-          const bool tin = tid < n;
-          sm.g[tid] = tin ? a.g[size_t(t0 + tid) * a.h_v + h] : 0.f;
-          sm.b[tid] = tin ? a.beta[size_t(t0 + tid) * a.h_v + h] : 0.f;
-        }
-      }
-      f32x4 vt;
+      const bool in = st_row < n;
+      const size_t qi = (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col;
+      kv = in ? load4<F32IN>(a.k, qi) : z4();
+      qv = in ? load4<F32IN>(a.q, qi) : z4();
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * h4 + r;
         vt[r] = row < n ? load1<F32IN>(a.v, (size_t(t0 + row) * a.h_v + h) * D + col) : 0.f;
       }
+      if (tid < L) {
+        const bool tin = tid < n;
+        gv = tin ? a.g[size_t(t0 + tid) * a.h_v + h] : 0.f;
+        bv = tin ? a.beta[size_t(t0 + tid) * a.h_v + h] : 0.f;
+      }
+    };
+    fetch(0);
+    for (int c = 0; c < nc; ++c) {
+      store_tile(hws + c * cstride, St);
+      *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
+      *reinterpret_cast<f32x4*>(&sm.q[st_row * S + st_col]) = qv;
+      if (tid < L) {
+        sm.g[tid] = gv;
+        sm.b[tid] = bv;
+      }
+      const f32x4 vc = vt;
       __syncthreads();
+      if (c + 1 < nc) fetch(c + 1);
       const Gates gt = make_gates(sm.g, sm.b, h4, i16);
       {
         const f32x4 ak = ld4(&sm.k[i16 * S + 16 * w + 4 * h4]);
+        const f32x4 aq = ld4(&sm.q[i16 * S + 16 * w + 4 * h4]);
         const f32x4 kkp = mm(ak, ak, z4());
+        const f32x4 qkp = mm(aq, ak, z4());
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.part[w][0][(4 * h4 + r) * L + i16] = kkp[r];
+        for (int r = 0; r < 4; ++r) {
+          sm.part[w][0][(4 * h4 + r) * L + i16] = kkp[r];
+          sm.part[w][1][(4 * h4 + r) * L + i16] = qkp[r];
+        }
       }
       f32x4 ks = z4();
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) ks = mm(ld4(&sm.k[i16 * S + 16 * rt + 4 * h4]), St[rt], ks);
       __syncthreads();
-      f32x4 kk = z4();
+      f32x4 kk = z4(), qk = z4();
 #pragma unroll
       for (int v = 0; v < NT; ++v)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) kk[r] += sm.part[v][0][(4 * h4 + r) * L + i16];
+        for (int r = 0; r < 4; ++r) {
+          kk[r] += sm.part[v][0][(4 * h4 + r) * L + i16];
+          qk[r] += sm.part[v][1][(4 * h4 + r) * L + i16];
+        }
       f32x4 T, Tt;
       solve(kk, gt, h4, i16, T, Tt);
+      if (w == 0) {  // the chunk's T, KK, QK for the backward pass
+        float* tp = tws + c * tstride;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = (4 * h4 + r) * L + i16;
+          tp[e] = T[r];
+          tp[L * L + e] = kk[r];
+          tp[2 * L * L + e] = qk[r];
+        }
+      }
       f32x4 R;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) R[r] = gt.bet[r] * (vt[r] - gt.gam[r] * ks[r]);
+      for (int r = 0; r < 4; ++r) R[r] = gt.bet[r] * (vc[r] - gt.gam[r] * ks[r]);
       const f32x4 U = mm(Tt, R, z4());
       const f32x4 dU = gt.del * U;
 #pragma unroll
@@ -299,27 +333,55 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     for (int rt = 0; rt < NT; ++rt) dS[rt] += x[rt];
   }
 
+  // Chunk c's T / T^T / KK / QK tiles and inputs, fetched one chunk ahead
+  // (the start state itself is loaded at the chunk top: holding it a chunk
+  // ahead costs more registers than the kernel has).
+  f32x4 Tn, Ttn, KKn, QKn, qv, kv, ov, vn;
+  float gv = 0.f, bv = 0.f;
+  auto fetch = [&](int c) {
+    const int t0 = t_beg + c * L;
+    const int n = min(L, t_end - t0);
+    const float* tp = tws + c * tstride;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = (4 * h4 + r) * L + i16;
+      Tn[r] = tp[e];
+      Ttn[r] = tp[i16 * L + 4 * h4 + r];
+      KKn[r] = tp[L * L + e];
+      QKn[r] = tp[2 * L * L + e];
+    }
+    const bool in = st_row < n;
+    const size_t qi = (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col;
+    const size_t oi = (size_t(t0 + st_row) * a.h_v + h) * D + st_col;
+    qv = in ? load4<F32IN>(a.q, qi) : z4();
+    kv = in ? load4<F32IN>(a.k, qi) : z4();
+    ov = in ? load4<F32IN>(a.dout, oi) : z4();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * h4 + r;
+      vn[r] = row < n ? load1<F32IN>(a.v, (size_t(t0 + row) * a.h_v + h) * D + col) : 0.f;
+    }
+    if (tid < L) {
+      const bool tin = tid < n;
+      gv = tin ? a.g[size_t(t0 + tid) * a.h_v + h] : 0.f;
+      bv = tin ? a.beta[size_t(t0 + tid) * a.h_v + h] : 0.f;
+    }
+  };
+  fetch(nc - 1);
+
   for (int c = nc - 1; c >= 0; --c) {
     const int t0 = t_beg + c * L;
     const int n = min(L, t_end - t0);
     const float* s0p = hws + c * cstride;
     f32x4 S0[NT];
     load_tile(s0p, S0);
-    {
-      const bool in = st_row < n;
-      const size_t qi = (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col;
-      const size_t oi = (size_t(t0 + st_row) * a.h_v + h) * D + st_col;
-      const f32x4 qv = in ? load4<F32IN>(a.q, qi) : z4();
-      const f32x4 kv = in ? load4<F32IN>(a.k, qi) : z4();
-      const f32x4 ov = in ? load4<F32IN>(a.dout, oi) * a.scale : z4();
-      *reinterpret_cast<f32x4*>(&sm.q[st_row * S + st_col]) = qv;
-      *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
-      *reinterpret_cast<f32x4*>(&sm.o[st_row * S + st_col]) = ov;
-      if (tid < L) {
-        const bool tin = tid < n;
-        sm.g[tid] = tin ? a.g[size_t(t0 + tid) * a.h_v + h] : 0.f;
-        sm.b[tid] = tin ? a.beta[size_t(t0 + tid) * a.h_v + h] : 0.f;
-      }
+    const f32x4 T = Tn, Tt = Ttn, kk = KKn, qk = QKn, vt = vn;
+    *reinterpret_cast<f32x4*>(&sm.q[st_row * S + st_col]) = qv;
+    *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
+    *reinterpret_cast<f32x4*>(&sm.o[st_row * S + st_col]) = ov * a.scale;
+    if (tid < L) {
+      sm.g[tid] = gv;
+      sm.b[tid] = bv;
     }
     {
       float* const dsw = &sm.ds[4 * h4 * S + col];
@@ -328,26 +390,9 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) dsw[(16 * rt + r) * S] = dS[rt][r];
     }
-    f32x4 vt;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * h4 + r;
-      vt[r] = row < n ? load1<F32IN>(a.v, (size_t(t0 + row) * a.h_v + h) * D + col) : 0.f;
-    }
     __syncthreads();  // chunk tensors and dS1 staged
 
     const Gates gt = make_gates(sm.g, sm.b, h4, i16);
-    {
-      const f32x4 ak = ld4(&sm.k[i16 * S + 16 * w + 4 * h4]);
-      const f32x4 aq = ld4(&sm.q[i16 * S + 16 * w + 4 * h4]);
-      const f32x4 kkp = mm(ak, ak, z4());
-      const f32x4 qkp = mm(aq, ak, z4());
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sm.part[w][0][(4 * h4 + r) * L + i16] = kkp[r];
-        sm.part[w][1][(4 * h4 + r) * L + i16] = qkp[r];
-      }
-    }
     f32x4 ks = z4(), qs = z4(), kd = z4();  // K S0, Q S0, K dS1 at column tile w
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
@@ -362,18 +407,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) glp += S0[rt][r] * dS[rt][r];
-    __syncthreads();  // KK, QK partials
 
-    f32x4 kk = z4(), qk = z4();
-#pragma unroll
-    for (int v = 0; v < NT; ++v)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        kk[r] += sm.part[v][0][(4 * h4 + r) * L + i16];
-        qk[r] += sm.part[v][1][(4 * h4 + r) * L + i16];
-      }
-    f32x4 T, Tt;
-    solve(kk, gt, h4, i16, T, Tt);
     f32x4 P, W0, R, dOc;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -499,6 +533,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
       dS[rt] = mm(aqt, gdo, gt.gam_last * dS[rt]);
       dS[rt] = mm(akt, gdv, dS[rt]);
     }
+    if (c > 0) fetch(c - 1);
     __syncthreads();  // every read of this chunk's tables done
 
     if (w == 0 && lane < L) {  // gate gradients of token i = lane

@@ -110,6 +110,7 @@ struct ScanBwdArgs {
   float* dbeta;          // [N, h_v]
   float* dinit;          // [n_roots, h_v, d, d] or null
   float* hws;            // workspace: chunk start states [max_level_chunks, h_v, d, d]
+  float* tws;            // workspace: chunk T, KK, QK [max_level_chunks, h_v, 3, 16, 16]
   float* dsseg;          // workspace: start-state gradients [n_seg, h_v, d, d]
   const int32_t* seg_off;
   const int32_t* parent;
