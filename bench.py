@@ -28,6 +28,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
+
+
+def scan_bwd_flops_per_token(s):
+    """Algorithmic flops per token of the scan backward: per value head, the
+    ten [16, d] x [d, d] contractions of a 16-token chunk (forward re-run:
+    K S0 and K^T U; backward: K S0, Q S0, K dS1, dO S0^T, dV S0^T, U dS1^T,
+    Q^T dO and K^T dV), 2 * 16 * d_k * d_v each, per 16 tokens; the
+    [16, 16]-sized products (about 14% more) are not counted."""
+    return s.h_v * 10 * 2 * s.d_k * s.d_v
 
 
 def scan_bytes_per_token(s):
@@ -120,7 +130,7 @@ def main():
                     help="scan schedule of the timed step (auto = the fork/rescan policy)")
     ap.add_argument("--no-rescan-compare", action="store_true",
                     help="skip the untimed-by-the-step comparison run of the rescan schedule")
-    ap.add_argument("--no-backward", action="store_true", help="skip the separately timed conv backward")
+    ap.add_argument("--no-backward", action="store_true", help="skip the separately timed conv and scan backward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="before timing, run one plain 1 GiB device copy (a counter reference for profiles)")
@@ -219,6 +229,30 @@ def main():
         bwd = {"tree_conv_backward": {"ms": bms, "bytes": bb, "GB/s": bb / bms / 1e6,
                                       "roofline_frac": bb / (HBM_PEAK_GBS * 1e9) / (bms * 1e-3), "reps": reps}}
         del dy, dx, bws
+        # The scan backward: do of the scan output -> dq, dk, dv, dg, dbeta,
+        # from the forward's segment states.
+        states = torch.empty((st["n_seg"], s.h_v, s.d_k, s.d_v), dtype=torch.float32, device=dev)
+        ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, out=o, states=states,
+                          schedule="level")
+        do = torch.empty_like(t["v"]).normal_()
+        sws = torch.empty(int(lib.tree_gdn_scan_backward_workspace_bytes(plan.handle, s.h_qk, s.h_v, s.d_k, s.d_v)),
+                          dtype=torch.uint8, device=dev)
+        sargs = (t["q"], t["k"], t["v"], t["g"], t["beta"], do, plan, states)
+        ptp.tree_gdn_scan_backward(*sargs, workspace=sws)
+        reps = 3
+        ev[0].record()
+        for _ in range(reps):
+            ptp.tree_gdn_scan_backward(*sargs, workspace=sws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        sms = ev[0].elapsed_time(ev[1]) / reps
+        fl = wl.n_tokens * scan_bwd_flops_per_token(s)
+        bwd["tree_gdn_scan_backward"] = {
+            "ms": sms, "unique_tokens_per_s": wl.n_tokens / sms * 1e3, "flops": fl, "TFLOP/s": fl / sms / 1e9,
+            "roofline": {"bound": "mfma", "dtype": "fp32", "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": fl / sms / 1e9 / FP32_MFMA_PEAK_TFLOPS},
+            "workspace_GiB": sws.numel() / 2**30, "reps": reps}
+        del states, do, sws
 
     n = wl.n_tokens
     state_bytes = 2 * st["n_parents"] * s.h_v * s.d_k * s.d_v * 4  # write + read once
