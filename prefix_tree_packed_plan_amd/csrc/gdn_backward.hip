@@ -56,6 +56,10 @@ namespace tg {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int L = 16;  // chunk length (tokens)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -73,6 +77,47 @@ __device__ __forceinline__ f32x4 mm(const f32x4 a, const f32x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 z4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- split-bf16 products (bf16 inputs) ------------------------------------------
+// An fp32 operand x is carried as hi + lo bf16 (x - hi - lo within 2^-18 |x|);
+// q, k and dO are exact in bf16.  A product of an exact operand with a split
+// one takes two MFMAs (hi, lo); of two split ones three (lo x lo dropped).
+// 16x16x32 operands: lane l supplies contraction indices kmap(h, e) =
+// e < 4 ? 4h + e : 16 + 4h + (e - 4), the same permutation on both sides, so
+// two accumulator row tiles (rows 4h + r and 16 + 4h + r) form one B operand.
+
+// Two floats -> two bf16 (round to nearest even), `a` in the low half.
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint2 pack4(const f32x4 x) { return make_uint2(pk2(x[0], x[1]), pk2(x[2], x[3])); }
+__device__ __forceinline__ void split4(const f32x4 x, uint2& hi, uint2& lo) {
+  const uint32_t h0 = pk2(x[0], x[1]), h1 = pk2(x[2], x[3]);
+  hi = make_uint2(h0, h1);
+  lo = make_uint2(pk2(x[0] - lo_f(h0), x[1] - hi_f(h0)), pk2(x[2] - lo_f(h1), x[3] - hi_f(h1)));
+}
+__device__ __forceinline__ uint4 cat(const uint2 a, const uint2 b) { return make_uint4(a.x, a.y, b.x, b.y); }
+// hi and lo of the 8 values (x0 = kmap entries 0..3, x1 = entries 4..7).
+__device__ __forceinline__ void split8(const f32x4 x0, const f32x4 x1, uint4& hi, uint4& lo) {
+  uint2 h0, l0, h1, l1;
+  split4(x0, h0, l0);
+  split4(x1, h1, l1);
+  hi = cat(h0, h1);
+  lo = cat(l0, l1);
+}
+__device__ __forceinline__ f32x4 mma32(const uint4 a, const uint4 b, const f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16b(const uint2 a, const uint2 b, const f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                   0, 0, 0);
+}
+// Exact (bf16-valued) A operand of a 32-deep contraction from an fp32 LDS row:
+// p points at column 4h of the block.
+__device__ __forceinline__ uint4 exact8(const float* p) { return cat(pack4(ld4(p)), pack4(ld4(p + 16))); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -282,8 +327,18 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
         }
       }
       f32x4 ks = z4();
+      if constexpr (F32IN) {
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt) ks = mm(ld4(&sm.k[i16 * S + 16 * rt + 4 * h4]), St[rt], ks);
+        for (int rt = 0; rt < NT; ++rt) ks = mm(ld4(&sm.k[i16 * S + 16 * rt + 4 * h4]), St[rt], ks);
+      } else {
+#pragma unroll
+        for (int m = 0; m < NT / 2; ++m) {
+          const uint4 ak = exact8(&sm.k[i16 * S + 32 * m + 4 * h4]);
+          uint4 bh, bl;
+          split8(St[2 * m], St[2 * m + 1], bh, bl);
+          ks = mma32(ak, bl, mma32(ak, bh, ks));
+        }
+      }
       __syncthreads();
       f32x4 kk = z4(), qk = z4();
 #pragma unroll
@@ -310,12 +365,19 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
       for (int r = 0; r < 4; ++r) R[r] = gt.bet[r] * (vc[r] - gt.gam[r] * ks[r]);
       const f32x4 U = mm(Tt, R, z4());
       const f32x4 dU = gt.del * U;
+      uint2 uh, ul;
+      if constexpr (!F32IN) split4(dU, uh, ul);
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
         f32x4 akt;
 #pragma unroll
         for (int s = 0; s < 4; ++s) akt[s] = sm.k[(4 * h4 + s) * S + 16 * rt + i16];
-        St[rt] = mm(akt, dU, gt.gam_last * St[rt]);
+        if constexpr (F32IN) {
+          St[rt] = mm(akt, dU, gt.gam_last * St[rt]);
+        } else {
+          const uint2 a = pack4(akt);
+          St[rt] = mma16b(a, ul, mma16b(a, uh, gt.gam_last * St[rt]));
+        }
       }
       __syncthreads();
     }
@@ -378,7 +440,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     const f32x4 T = Tn, Tt = Ttn, kk = KKn, qk = QKn, vt = vn;
     *reinterpret_cast<f32x4*>(&sm.q[st_row * S + st_col]) = qv;
     *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
-    *reinterpret_cast<f32x4*>(&sm.o[st_row * S + st_col]) = ov * a.scale;
+    *reinterpret_cast<f32x4*>(&sm.o[st_row * S + st_col]) = F32IN ? ov * a.scale : ov;
     if (tid < L) {
       sm.g[tid] = gv;
       sm.b[tid] = bv;
@@ -394,13 +456,27 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 
     const Gates gt = make_gates(sm.g, sm.b, h4, i16);
     f32x4 ks = z4(), qs = z4(), kd = z4();  // K S0, Q S0, K dS1 at column tile w
+    if constexpr (F32IN) {
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      const f32x4 ak = ld4(&sm.k[i16 * S + 16 * rt + 4 * h4]);
-      const f32x4 aq = ld4(&sm.q[i16 * S + 16 * rt + 4 * h4]);
-      ks = mm(ak, S0[rt], ks);
-      qs = mm(aq, S0[rt], qs);
-      kd = mm(ak, dS[rt], kd);
+      for (int rt = 0; rt < NT; ++rt) {
+        const f32x4 ak = ld4(&sm.k[i16 * S + 16 * rt + 4 * h4]);
+        const f32x4 aq = ld4(&sm.q[i16 * S + 16 * rt + 4 * h4]);
+        ks = mm(ak, S0[rt], ks);
+        qs = mm(aq, S0[rt], qs);
+        kd = mm(ak, dS[rt], kd);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NT / 2; ++m) {
+        const uint4 ak = exact8(&sm.k[i16 * S + 32 * m + 4 * h4]);
+        const uint4 aq = exact8(&sm.q[i16 * S + 32 * m + 4 * h4]);
+        uint4 sh, sl, dh, dl;
+        split8(S0[2 * m], S0[2 * m + 1], sh, sl);
+        split8(dS[2 * m], dS[2 * m + 1], dh, dl);
+        ks = mma32(ak, sl, mma32(ak, sh, ks));
+        qs = mma32(aq, sl, mma32(aq, sh, qs));
+        kd = mma32(ak, dl, mma32(ak, dh, kd));
+      }
     }
     float glp = 0.f;
 #pragma unroll
@@ -415,7 +491,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
       P[r] = row >= i16 ? qk[r] * gt.Gm[r] : 0.f;
       W0[r] = vt[r] - gt.gam[r] * ks[r];
       R[r] = gt.bet[r] * W0[r];
-      dOc[r] = sm.o[row * S + col];
+      dOc[r] = F32IN ? sm.o[row * S + col] : sm.o[row * S + col] * a.scale;
     }
     const f32x4 U = mm(Tt, R, z4());
     const f32x4 dU = mm(P, dOc, gt.del * kd);
@@ -453,7 +529,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
       const f32x4 ar = ld4(&sm.r[i16 * S + 16 * w + 4 * h4]);
       const f32x4 ao = ld4(&sm.o[i16 * S + 16 * w + 4 * h4]);
       const f32x4 dap = mm(ar, au, z4());  // dR U^T over this wave's columns
-      const f32x4 dpp_ = mm(ao, au, z4());  // dOs U^T
+      const f32x4 dpp_ = mm(ao, au, z4()) * (F32IN ? 1.f : a.scale);  // dOs U^T
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         sm.part[w][0][(4 * h4 + r) * L + i16] = dap[r];
@@ -501,12 +577,29 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     }
     f32x4 xo = z4(), xv = z4(), xu = z4();  // dOs S0^T, dV S0^T, diag(delta) U dS1^T
     const float* const dsr = &sm.ds[(16 * w + i16) * S + 4 * h4];
+    if constexpr (F32IN) {
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) {
-      const int o4 = i16 * S + 16 * jt + 4 * h4;
-      xo = mm(ld4(&sm.o[o4]), S0row[jt], xo);
-      xv = mm(gt.bet_c * ld4(&sm.r[o4]), S0row[jt], xv);
-      xu = mm(gt.del_c * ld4(&sm.u[o4]), ld4(dsr + 16 * jt), xu);
+      for (int jt = 0; jt < NT; ++jt) {
+        const int o4 = i16 * S + 16 * jt + 4 * h4;
+        xo = mm(ld4(&sm.o[o4]), S0row[jt], xo);
+        xv = mm(gt.bet_c * ld4(&sm.r[o4]), S0row[jt], xv);
+        xu = mm(gt.del_c * ld4(&sm.u[o4]), ld4(dsr + 16 * jt), xu);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NT / 2; ++m) {
+        const int o4 = i16 * S + 32 * m + 4 * h4;
+        uint4 sh, sl, dh, dl, vh, vl, uh, ul;
+        split8(S0row[2 * m], S0row[2 * m + 1], sh, sl);
+        split8(ld4(dsr + 32 * m), ld4(dsr + 32 * m + 16), dh, dl);
+        split8(gt.bet_c * ld4(&sm.r[o4]), gt.bet_c * ld4(&sm.r[o4 + 16]), vh, vl);
+        split8(gt.del_c * ld4(&sm.u[o4]), gt.del_c * ld4(&sm.u[o4 + 16]), uh, ul);
+        const uint4 ao = exact8(&sm.o[o4]);
+        xo = mma32(ao, sl, mma32(ao, sh, xo));
+        xv = mma32(vl, sh, mma32(vh, sl, mma32(vh, sh, xv)));
+        xu = mma32(ul, dh, mma32(uh, dl, mma32(uh, dh, xu)));
+      }
+      xo = xo * a.scale;
     }
     const f32x4 dQ = gt.gam * xo + mm(dQKPt, kc, z4());
     f32x4 dK = mm(dQKP, qc, z4());
@@ -522,6 +615,8 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
       }
     }
     const f32x4 gdo = gt.gam * dOc, gdv = -(gt.gam * dV);
+    uint4 gh, gl;  // [diag(gamma) dOs; -diag(gamma) dV] as one 32-deep B operand
+    if constexpr (!F32IN) split8(gdo, gdv, gh, gl);
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       f32x4 aqt, akt;
@@ -530,8 +625,13 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
         aqt[s] = sm.q[(4 * h4 + s) * S + 16 * rt + i16];
         akt[s] = sm.k[(4 * h4 + s) * S + 16 * rt + i16];
       }
-      dS[rt] = mm(aqt, gdo, gt.gam_last * dS[rt]);
-      dS[rt] = mm(akt, gdv, dS[rt]);
+      if constexpr (F32IN) {
+        dS[rt] = mm(aqt, gdo, gt.gam_last * dS[rt]);
+        dS[rt] = mm(akt, gdv, dS[rt]);
+      } else {
+        const uint4 a = cat(pack4(aqt), pack4(akt));  // [Q^T | K^T]
+        dS[rt] = mma32(a, gl, mma32(a, gh, gt.gam_last * dS[rt]));
+      }
     }
     if (c > 0) fetch(c - 1);
     __syncthreads();  // every read of this chunk's tables done
