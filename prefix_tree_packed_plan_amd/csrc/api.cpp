@@ -289,7 +289,7 @@ size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h
   const tg::Plan& p = plan->p;
   const size_t dd = static_cast<size_t>(d_k) * d_v;
   size_t n = (static_cast<size_t>(p.max_level_chunks) + p.n_seg) * h_v * dd;
-  n += static_cast<size_t>(p.max_level_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
+  n += static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
   if (h_v != h_qk) n += 2 * static_cast<size_t>(p.n_tokens) * h_v * d_k;
   return n * sizeof(float);
 }
@@ -337,7 +337,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.hws = static_cast<float*>(ws);
   a.dsseg = a.hws + static_cast<size_t>(p.max_level_chunks) * h_v * dd;
   a.tws = a.dsseg + static_cast<size_t>(p.n_seg) * h_v * dd;
-  float* per_head = a.tws + static_cast<size_t>(p.max_level_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
+  float* per_head = a.tws + static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
   const bool grouped = h_v != h_qk;
   a.dq = grouped ? per_head : dq;
   a.dk = grouped ? per_head + static_cast<size_t>(n_tokens) * h_v * d_k : dk;
@@ -348,10 +348,17 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.kid_off = base + p.m_kid_off;
   a.kid = base + p.m_kid;
   a.bchunk = base + p.m_bchunk;
+  a.gchunk = base + p.m_gchunk;
+  a.chunk_seg = base + p.m_chunk_seg;
+  a.n_chunks = static_cast<int32_t>(p.total_chunks);
   a.h_qk = h_qk;
   a.h_v = h_v;
   a.scale = scale;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  {
+    const hipError_t e = tg::launch_scan_backward_prep(a, d_k, dtype, st);
+    if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);
+  }
   // Deepest level first: a parent sums its children's start-state gradients.
   for (int32_t l = p.n_levels - 1; l >= 0; --l) {
     a.items = base + p.m_order + p.level_start[l];

@@ -143,7 +143,11 @@ struct BwdSmem {
   alignas(16) float gl[NW][4];          // per-wave partial sum(S0 o dS1)
   alignas(16) float rows[NW][3][L];     // per-wave partial row sums
   alignas(16) float m[2][L * 17];       // M and dA o KK o Gamma
-  alignas(16) float part[NW][2][L * L];  // per-wave 16x16 partial products
+  // Per-wave 16x16 partials (dR U^T, dOs U^T): part in the lanes'
+  // accumulator order (lane l's 4 values at 4l), part_t the transpose in the
+  // same order, so that either orientation is one 16-byte read per lane.
+  alignas(16) float part[NW][2][L * L];
+  alignas(16) float part_t[NW][2][L * L];
   alignas(16) float q[L * S];
   alignas(16) float k[L * S];
   alignas(16) float o[L * S];  // scale * dO
@@ -246,10 +250,10 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
   const size_t DD = size_t(D) * D;
   const size_t cstride = size_t(a.h_v) * DD;  // between consecutive chunks in the workspace
   float* hws = a.hws + (size_t(a.bchunk[seg]) * a.h_v + h) * DD;
-  // T, KK and QK of every chunk, [16, 16] fp32 each.
+  // T, KK and QK of every chunk (from the prep kernel), [16, 16] fp32 each.
   constexpr int TW = 3 * L * L;
   const size_t tstride = size_t(a.h_v) * TW;
-  float* tws = a.tws + (size_t(a.bchunk[seg]) * a.h_v + h) * TW;
+  const float* tws = a.tws + (size_t(a.gchunk[seg]) * a.h_v + h) * TW;
   const int dq_head = a.dq_heads == a.h_v ? h : hq;
 
   // Staging: thread -> (row, 4 columns) of a [16, d] chunk tensor.
@@ -268,6 +272,18 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) p[size_t(16 * rt + 4 * h4 + r) * D + col] = x[rt][r];
   };
+  // Chunk start states in the workspace are stored as 16x16 tiles (row tile
+  // rt, column tile ct at (rt * NT + ct) * 256 floats), each in the lanes'
+  // accumulator order (lane l's 4 values at 4l): one 16-byte access per lane
+  // and tile.
+  auto store_ws = [&](float* p, const f32x4 (&x)[NT]) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) *reinterpret_cast<f32x4*>(p + (rt * NT + w) * 256 + 4 * lane) = x[rt];
+  };
+  auto load_ws = [&](const float* p, f32x4 (&x)[NT]) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) x[rt] = ld4(p + (rt * NT + w) * 256 + 4 * lane);
+  };
 
   // ---- pass 1: chunk start states --------------------------------------------
   {
@@ -281,20 +297,19 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) St[rt] = z4();
     }
-    // Inputs of chunk c in registers, fetched one chunk ahead.
-    f32x4 kv, qv, vt;
+    // Inputs and T^T of chunk c in registers, fetched one chunk ahead.
+    f32x4 kv, vt, Ttn;
     float gv = 0.f, bv = 0.f;
     auto fetch = [&](int c) {
       const int t0 = t_beg + c * L;
       const int n = min(L, t_end - t0);
       const bool in = st_row < n;
-      const size_t qi = (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col;
-      kv = in ? load4<F32IN>(a.k, qi) : z4();
-      qv = in ? load4<F32IN>(a.q, qi) : z4();
+      kv = in ? load4<F32IN>(a.k, (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col) : z4();
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * h4 + r;
         vt[r] = row < n ? load1<F32IN>(a.v, (size_t(t0 + row) * a.h_v + h) * D + col) : 0.f;
+        Ttn[r] = tws[c * tstride + i16 * L + row];
       }
       if (tid < L) {
         const bool tin = tid < n;
@@ -304,28 +319,16 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     };
     fetch(0);
     for (int c = 0; c < nc; ++c) {
-      store_tile(hws + c * cstride, St);
+      store_ws(hws + c * cstride, St);
       *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
-      *reinterpret_cast<f32x4*>(&sm.q[st_row * S + st_col]) = qv;
       if (tid < L) {
         sm.g[tid] = gv;
         sm.b[tid] = bv;
       }
-      const f32x4 vc = vt;
+      const f32x4 vc = vt, Tt = Ttn;
       __syncthreads();
       if (c + 1 < nc) fetch(c + 1);
       const Gates gt = make_gates(sm.g, sm.b, h4, i16);
-      {
-        const f32x4 ak = ld4(&sm.k[i16 * S + 16 * w + 4 * h4]);
-        const f32x4 aq = ld4(&sm.q[i16 * S + 16 * w + 4 * h4]);
-        const f32x4 kkp = mm(ak, ak, z4());
-        const f32x4 qkp = mm(aq, ak, z4());
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sm.part[w][0][(4 * h4 + r) * L + i16] = kkp[r];
-          sm.part[w][1][(4 * h4 + r) * L + i16] = qkp[r];
-        }
-      }
       f32x4 ks = z4();
       if constexpr (F32IN) {
 #pragma unroll
@@ -337,27 +340,6 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
           uint4 bh, bl;
           split8(St[2 * m], St[2 * m + 1], bh, bl);
           ks = mma32(ak, bl, mma32(ak, bh, ks));
-        }
-      }
-      __syncthreads();
-      f32x4 kk = z4(), qk = z4();
-#pragma unroll
-      for (int v = 0; v < NT; ++v)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          kk[r] += sm.part[v][0][(4 * h4 + r) * L + i16];
-          qk[r] += sm.part[v][1][(4 * h4 + r) * L + i16];
-        }
-      f32x4 T, Tt;
-      solve(kk, gt, h4, i16, T, Tt);
-      if (w == 0) {  // the chunk's T, KK, QK for the backward pass
-        float* tp = tws + c * tstride;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = (4 * h4 + r) * L + i16;
-          tp[e] = T[r];
-          tp[L * L + e] = kk[r];
-          tp[2 * L * L + e] = qk[r];
         }
       }
       f32x4 R;
@@ -436,7 +418,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     const int n = min(L, t_end - t0);
     const float* s0p = hws + c * cstride;
     f32x4 S0[NT];
-    load_tile(s0p, S0);
+    load_ws(s0p, S0);
     const f32x4 T = Tn, Tt = Ttn, kk = KKn, qk = QKn, vt = vn;
     *reinterpret_cast<f32x4*>(&sm.q[st_row * S + st_col]) = qv;
     *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
@@ -520,20 +502,30 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     }
     __syncthreads();  // U, dR staged
 
-    // S0 rows 16w .. 16w+15 as the B operand of products with S0^T.
+    // S0 rows 16w .. 16w+15 as the B operand of products with S0^T:
+    // S0row[jt][e] = S0[16w + i][16jt + 4h + e], from tile (w, jt).
     f32x4 S0row[NT];
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) S0row[jt] = ld4(s0p + size_t(16 * w + i16) * D + 16 * jt + 4 * h4);
+    for (int jt = 0; jt < NT; ++jt) {
+      const float* tp = s0p + (w * NT + jt) * 256 + 4 * (16 * (i16 >> 2) + 4 * h4) + (i16 & 3);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S0row[jt][e] = tp[4 * e];
+    }
     {
       const f32x4 au = ld4(&sm.u[i16 * S + 16 * w + 4 * h4]);
       const f32x4 ar = ld4(&sm.r[i16 * S + 16 * w + 4 * h4]);
       const f32x4 ao = ld4(&sm.o[i16 * S + 16 * w + 4 * h4]);
       const f32x4 dap = mm(ar, au, z4());  // dR U^T over this wave's columns
       const f32x4 dpp_ = mm(ao, au, z4()) * (F32IN ? 1.f : a.scale);  // dOs U^T
+      *reinterpret_cast<f32x4*>(&sm.part[w][0][4 * lane]) = dap;
+      *reinterpret_cast<f32x4*>(&sm.part[w][1][4 * lane]) = dpp_;
+      // Element (row 4h + r, column i) of the transpose is read by lane
+      // 16 (i / 4) + 4h + r as its value i % 4.
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sm.part[w][0][(4 * h4 + r) * L + i16] = dap[r];
-        sm.part[w][1][(4 * h4 + r) * L + i16] = dpp_[r];
+        const int e = 4 * (16 * (i16 >> 2) + 4 * h4 + r) + (i16 & 3);
+        sm.part_t[w][0][e] = dap[r];
+        sm.part_t[w][1][e] = dpp_[r];
       }
     }
     __syncthreads();  // dA, dP partials
@@ -542,14 +534,12 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     {
       f32x4 x = z4(), xt = z4(), y = z4(), yt = z4();
 #pragma unroll
-      for (int v = 0; v < NT; ++v)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] += sm.part[v][0][(4 * h4 + r) * L + i16];
-          xt[r] += sm.part[v][0][i16 * L + 4 * h4 + r];
-          y[r] += sm.part[v][1][(4 * h4 + r) * L + i16];
-          yt[r] += sm.part[v][1][i16 * L + 4 * h4 + r];
-        }
+      for (int v = 0; v < NT; ++v) {
+        x += ld4(&sm.part[v][0][4 * lane]);
+        xt += ld4(&sm.part_t[v][0][4 * lane]);
+        y += ld4(&sm.part[v][1][4 * lane]);
+        yt += ld4(&sm.part_t[v][1][4 * lane]);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * h4 + r;
@@ -680,6 +670,66 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
   }
 }
 
+// T = (I + A)^-1, KK and QK of every chunk and value head: state-free, so
+// all chunks of the trie run in parallel before the level launches.  One
+// wave per (chunk, value head); tokens past a segment's end are zero rows
+// with g = beta = 0, as in the level kernel.
+template <int D, bool F32IN>
+__global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(ScanBwdArgs a) {
+  __shared__ float sg[4][L], sb[4][L];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int h4 = lane >> 4;
+  const int i16 = lane & 15;
+  const int64_t item = int64_t(blockIdx.x) * 4 + w;
+  const bool live = item < int64_t(a.n_chunks) * a.h_v;
+  const int c = live ? int(item / a.h_v) : 0;
+  const int h = live ? int(item - int64_t(c) * a.h_v) : 0;
+  const int seg = a.chunk_seg[c];
+  const int hq = h / (a.h_v / a.h_qk);
+  const int t0 = a.seg_off[seg] + (c - a.gchunk[seg]) * L;
+  const int n = live ? min(L, a.seg_off[seg + 1] - t0) : 0;
+  if (lane < L) {
+    const bool tin = lane < n;
+    sg[w][lane] = tin ? a.g[size_t(t0 + lane) * a.h_v + h] : 0.f;
+    sb[w][lane] = tin ? a.beta[size_t(t0 + lane) * a.h_v + h] : 0.f;
+  }
+  const bool rin = i16 < n;
+  const size_t rbase = (size_t(t0 + (rin ? i16 : 0)) * a.h_qk + hq) * D;
+  f32x4 kk = z4(), qk = z4();
+  if constexpr (F32IN) {
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+      const f32x4 ak = rin ? load4<true>(a.k, rbase + 16 * m + 4 * h4) : z4();
+      const f32x4 aq = rin ? load4<true>(a.q, rbase + 16 * m + 4 * h4) : z4();
+      kk = mm(ak, ak, kk);
+      qk = mm(aq, ak, qk);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+      const size_t i0 = rbase + 32 * m + 4 * h4;
+      const uint4 ak = rin ? cat(pack4(load4<false>(a.k, i0)), pack4(load4<false>(a.k, i0 + 16))) : make_uint4(0, 0, 0, 0);
+      const uint4 aq = rin ? cat(pack4(load4<false>(a.q, i0)), pack4(load4<false>(a.q, i0 + 16))) : make_uint4(0, 0, 0, 0);
+      kk = mma32(ak, ak, kk);  // bf16 x bf16 products are exact in fp32
+      qk = mma32(aq, ak, qk);
+    }
+  }
+  __syncthreads();
+  const Gates gt = make_gates(sg[w], sb[w], h4, i16);
+  f32x4 T, Tt;
+  solve(kk, gt, h4, i16, T, Tt);
+  if (!live) return;
+  float* tp = a.tws + (size_t(c) * a.h_v + h) * (3 * L * L);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int e = (4 * h4 + r) * L + i16;
+    tp[e] = T[r];
+    tp[L * L + e] = kk[r];
+    tp[2 * L * L + e] = qk[r];
+  }
+}
+
 // dst[t, j, :] = sum over the G value heads of q/k head j of src[t, j G + m, :],
 // in head order.
 __global__ void head_group_sum(const float* __restrict__ src, float* __restrict__ dst, int64_t n_out4, int G,
@@ -701,10 +751,28 @@ hipError_t launch_bwd_level(const ScanBwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool F32IN>
+hipError_t launch_prep(const ScanBwdArgs& a, hipStream_t stream) {
+  const int64_t items = int64_t(a.n_chunks) * a.h_v;
+  if (items <= 0) return hipSuccess;
+  gdn_bwd_prep_kernel<D, F32IN><<<dim3(unsigned((items + 3) / 4)), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool scan_backward_supported(int d_k, int d_v, int dtype) {
   return d_k == d_v && (d_k == 32 || d_k == 64 || d_k == 128) && (dtype == TREE_DTYPE_BF16 || dtype == TREE_DTYPE_F32);
+}
+
+hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream) {
+  const bool f32 = dtype == TREE_DTYPE_F32;
+  switch (d) {
+    case 32: return f32 ? launch_prep<32, true>(a, stream) : launch_prep<32, false>(a, stream);
+    case 64: return f32 ? launch_prep<64, true>(a, stream) : launch_prep<64, false>(a, stream);
+    case 128: return f32 ? launch_prep<128, true>(a, stream) : launch_prep<128, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream) {

@@ -110,7 +110,7 @@ struct ScanBwdArgs {
   float* dbeta;          // [N, h_v]
   float* dinit;          // [n_roots, h_v, d, d] or null
   float* hws;            // workspace: chunk start states [max_level_chunks, h_v, d, d]
-  float* tws;            // workspace: chunk T, KK, QK [max_level_chunks, h_v, 3, 16, 16]
+  float* tws;            // workspace: chunk T, KK, QK [total_chunks, h_v, 3, 16, 16]
   float* dsseg;          // workspace: start-state gradients [n_seg, h_v, d, d]
   const int32_t* seg_off;
   const int32_t* parent;
@@ -118,6 +118,9 @@ struct ScanBwdArgs {
   const int32_t* kid_off;
   const int32_t* kid;
   const int32_t* bchunk;
+  const int32_t* gchunk;
+  const int32_t* chunk_seg;
+  int32_t n_chunks;      // total chunks (prep launch)
   const int32_t* items;  // segments of this level
   int32_t n_items;
   int32_t h_qk;
@@ -126,7 +129,9 @@ struct ScanBwdArgs {
   float scale;
 };
 
-// Scan backward over one trie level (gdn_backward.hip); d = d_k = d_v.
+// Scan backward (gdn_backward.hip); d = d_k = d_v.  The prep launch computes
+// every chunk's T, KK and QK (state-free); then one launch per trie level.
+hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream);
 hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream);
 // dst[t, j] = sum_m src[t, j group + m] over [n_tok, h_qk * group, d] fp32.
 hipError_t launch_head_group_sum(const float* src, float* dst, int64_t n_tok, int h_qk, int group, int d,

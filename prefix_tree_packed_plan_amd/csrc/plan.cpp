@@ -226,6 +226,13 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
     }
     p.max_level_chunks = std::max(p.max_level_chunks, c);
   }
+  p.gchunk.assign(n_seg, 0);
+  for (int32_t i = 0; i < n_seg; ++i) {
+    p.gchunk[i] = static_cast<int32_t>(p.total_chunks);
+    const int32_t nc = (p.lens[i] + Plan::kBwdChunk - 1) / Plan::kBwdChunk;
+    for (int32_t j = 0; j < nc; ++j) p.chunk_seg.push_back(i);
+    p.total_chunks += nc;
+  }
 
   // Device mirror.
   p.m_seg_off = 0;
@@ -245,7 +252,9 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   p.m_kid_off = p.m_roots + p.roots.size();
   p.m_kid = p.m_kid_off + p.kid_off.size();
   p.m_bchunk = p.m_kid + p.kid.size();
-  p.mirror.resize(p.m_bchunk + p.bchunk.size());
+  p.m_gchunk = p.m_bchunk + p.bchunk.size();
+  p.m_chunk_seg = p.m_gchunk + p.gchunk.size();
+  p.mirror.resize(p.m_chunk_seg + p.chunk_seg.size());
   std::copy(p.seg_off.begin(), p.seg_off.end(), p.mirror.begin() + p.m_seg_off);
   std::copy(p.parents.begin(), p.parents.end(), p.mirror.begin() + p.m_parent);
   std::copy(p.slot.begin(), p.slot.end(), p.mirror.begin() + p.m_slot);
@@ -263,6 +272,8 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   std::copy(p.kid_off.begin(), p.kid_off.end(), p.mirror.begin() + p.m_kid_off);
   std::copy(p.kid.begin(), p.kid.end(), p.mirror.begin() + p.m_kid);
   std::copy(p.bchunk.begin(), p.bchunk.end(), p.mirror.begin() + p.m_bchunk);
+  std::copy(p.gchunk.begin(), p.gchunk.end(), p.mirror.begin() + p.m_gchunk);
+  std::copy(p.chunk_seg.begin(), p.chunk_seg.end(), p.mirror.begin() + p.m_chunk_seg);
 
   *out = std::move(p);
   return TREE_OK;
