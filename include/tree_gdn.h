@@ -304,10 +304,10 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g,
 
 /*
  * tree_gdn_scan_backward_workspace_bytes -- device workspace
- * tree_gdn_scan_backward needs: the start state ([h_v, d_k, d_v] fp32) of
- * every 16-token chunk of the largest trie level, three [h_v, 16, 16] fp32
- * matrices of every chunk, one start-state gradient ([h_v, d_k, d_v] fp32)
- * per segment, plus per-value-head dq and dk
+ * tree_gdn_scan_backward needs: the start state ([h_v, d_k, d_v] fp32) and
+ * three [h_v, 16, 16] fp32 matrices of every 16-token chunk, one
+ * start-state gradient ([h_v, d_k, d_v] fp32) per segment, plus
+ * per-value-head dq and dk
  * ([n_tokens, h_v, d_k] fp32 each) when h_v != h_qk.
  */
 size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h_qk, int32_t h_v, int32_t d_k,

@@ -288,7 +288,7 @@ size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h
   if (!plan || h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0) return 0;
   const tg::Plan& p = plan->p;
   const size_t dd = static_cast<size_t>(d_k) * d_v;
-  size_t n = (static_cast<size_t>(p.max_level_chunks) + p.n_seg) * h_v * dd;
+  size_t n = (static_cast<size_t>(p.total_chunks) + p.n_seg) * h_v * dd;
   n += static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
   if (h_v != h_qk) n += 2 * static_cast<size_t>(p.n_tokens) * h_v * d_k;
   return n * sizeof(float);
@@ -335,7 +335,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.dbeta = dbeta;
   a.dinit = dinit_states;
   a.hws = static_cast<float*>(ws);
-  a.dsseg = a.hws + static_cast<size_t>(p.max_level_chunks) * h_v * dd;
+  a.dsseg = a.hws + static_cast<size_t>(p.total_chunks) * h_v * dd;
   a.tws = a.dsseg + static_cast<size_t>(p.n_seg) * h_v * dd;
   float* per_head = a.tws + static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
   const bool grouped = h_v != h_qk;
@@ -351,6 +351,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.gchunk = base + p.m_gchunk;
   a.chunk_seg = base + p.m_chunk_seg;
   a.n_chunks = static_cast<int32_t>(p.total_chunks);
+  a.n_seg = p.n_seg;
   a.h_qk = h_qk;
   a.h_v = h_v;
   a.scale = scale;

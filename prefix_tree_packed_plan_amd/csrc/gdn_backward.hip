@@ -34,12 +34,15 @@
 // (I + A)^-1 for the nilpotent A is the product
 // (I + N)(I + N^2)(I + N^4)(I + N^8), N = -A: six 16x16 MFMA products.
 //
-// Work item: one segment and one value head per work-group of d/16 waves.
-// Pass 1 re-runs the segment's chunks forward from the parent's final state
-// (the forward's `states`) and writes every chunk's start state to the
-// workspace; pass 2 walks the chunks backwards.  Wave w owns column tile w
-// (16 columns) of every [16, d] chunk tensor and of the state gradient dS,
-// which stays in MFMA accumulator registers across the segment.
+// Launches: a prep kernel computes every chunk's T, KK and QK (state-free, all
+// chunks at once); a states kernel re-runs every segment forward from its
+// parent's final state (the forward's `states`; all segments at once) and
+// writes every chunk's start state to the workspace; then one launch per
+// trie level, deepest first, walks each segment's chunks backwards.  Work
+// item: one segment and one value head per work-group of d/16 waves; wave w
+// owns column tile w (16 columns) of every [16, d] chunk tensor and of the
+// state gradient dS, which stays in MFMA accumulator registers across the
+// segment.
 //
 // MFMA: v_mfma_f32_16x16x4_f32 (fp32 inputs, fp32 accumulate) throughout.
 // Lane l = 16 h + i (h = l / 16) holds accumulator rows 4h + r, column i.
@@ -227,65 +230,55 @@ __device__ __forceinline__ float load1(const void* base, size_t idx) {
   return __uint_as_float(uint32_t(static_cast<const uint16_t*>(base)[idx]) << 16);
 }
 
-template <int D, bool F32IN>
-__global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
-  constexpr int NT = D / 16;  // row tiles of the state = waves
-  constexpr int S = D + 4;
-  using SM = BwdSmem<D>;
-  __shared__ SM sm;
+// Forward re-run: every chunk's start state, for all segments at once (a
+// segment starts from its parent's final state, which the forward already
+// wrote), into the workspace as 16x16 tiles (row tile rt, column tile ct at
+// (rt * NT + ct) * 256 floats), each in the lanes' accumulator order (lane
+// l's 4 values at 4l): one 16-byte store per lane and tile.  Few registers,
+// so two work-groups share a compute unit.
+template <int D>
+struct StatesSmem {
+  static constexpr int S = D + 4;
+  alignas(16) float g[L];
+  alignas(16) float b[L];
+  alignas(16) float k[L * S];
+};
 
+template <int D, bool F32IN>
+__global__ __launch_bounds__(4 * D, 2) void gdn_bwd_states_kernel(ScanBwdArgs a) {
+  constexpr int NT = D / 16;
+  constexpr int S = D + 4;
+  __shared__ StatesSmem<D> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int h4 = lane >> 4;
   const int i16 = lane & 15;
   const int col = 16 * w + i16;
-
-  const int item = blockIdx.x / a.h_v;
-  const int h = blockIdx.x - item * a.h_v;
-  const int seg = a.items[item];
+  const int seg = blockIdx.x / a.h_v;
+  const int h = blockIdx.x - seg * a.h_v;
   const int hq = h / (a.h_v / a.h_qk);
   const int t_beg = a.seg_off[seg], t_end = a.seg_off[seg + 1];
   const int nc = (t_end - t_beg + L - 1) / L;
   const size_t DD = size_t(D) * D;
-  const size_t cstride = size_t(a.h_v) * DD;  // between consecutive chunks in the workspace
-  float* hws = a.hws + (size_t(a.bchunk[seg]) * a.h_v + h) * DD;
-  // T, KK and QK of every chunk (from the prep kernel), [16, 16] fp32 each.
+  const size_t cstride = size_t(a.h_v) * DD;
+  float* hws = a.hws + (size_t(a.gchunk[seg]) * a.h_v + h) * DD;
   constexpr int TW = 3 * L * L;
   const size_t tstride = size_t(a.h_v) * TW;
   const float* tws = a.tws + (size_t(a.gchunk[seg]) * a.h_v + h) * TW;
-  const int dq_head = a.dq_heads == a.h_v ? h : hq;
-
-  // Staging: thread -> (row, 4 columns) of a [16, d] chunk tensor.
   const int st_row = tid / (D / 4);
   const int st_col = 4 * (tid % (D / 4));
-
   auto load_tile = [&](const float* p, f32x4 (&x)[NT]) {
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[rt][r] = p[size_t(16 * rt + 4 * h4 + r) * D + col];
   };
-  auto store_tile = [&](float* p, const f32x4 (&x)[NT]) {
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[size_t(16 * rt + 4 * h4 + r) * D + col] = x[rt][r];
-  };
-  // Chunk start states in the workspace are stored as 16x16 tiles (row tile
-  // rt, column tile ct at (rt * NT + ct) * 256 floats), each in the lanes'
-  // accumulator order (lane l's 4 values at 4l): one 16-byte access per lane
-  // and tile.
   auto store_ws = [&](float* p, const f32x4 (&x)[NT]) {
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) *reinterpret_cast<f32x4*>(p + (rt * NT + w) * 256 + 4 * lane) = x[rt];
   };
-  auto load_ws = [&](const float* p, f32x4 (&x)[NT]) {
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) x[rt] = ld4(p + (rt * NT + w) * 256 + 4 * lane);
-  };
 
-  // ---- pass 1: chunk start states --------------------------------------------
   {
     f32x4 St[NT];
     const int par = a.parent[seg];
@@ -364,6 +357,59 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
       __syncthreads();
     }
   }
+
+}
+
+template <int D, bool F32IN>
+__global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
+  constexpr int NT = D / 16;  // row tiles of the state = waves
+  constexpr int S = D + 4;
+  using SM = BwdSmem<D>;
+  __shared__ SM sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h4 = lane >> 4;
+  const int i16 = lane & 15;
+  const int col = 16 * w + i16;
+
+  const int item = blockIdx.x / a.h_v;
+  const int h = blockIdx.x - item * a.h_v;
+  const int seg = a.items[item];
+  const int hq = h / (a.h_v / a.h_qk);
+  const int t_beg = a.seg_off[seg], t_end = a.seg_off[seg + 1];
+  const int nc = (t_end - t_beg + L - 1) / L;
+  const size_t DD = size_t(D) * D;
+  const size_t cstride = size_t(a.h_v) * DD;  // between consecutive chunks in the workspace
+  const float* hws = a.hws + (size_t(a.gchunk[seg]) * a.h_v + h) * DD;
+  // T, KK and QK of every chunk (from the prep kernel), [16, 16] fp32 each.
+  constexpr int TW = 3 * L * L;
+  const size_t tstride = size_t(a.h_v) * TW;
+  const float* tws = a.tws + (size_t(a.gchunk[seg]) * a.h_v + h) * TW;
+  const int dq_head = a.dq_heads == a.h_v ? h : hq;
+
+  // Staging: thread -> (row, 4 columns) of a [16, d] chunk tensor.
+  const int st_row = tid / (D / 4);
+  const int st_col = 4 * (tid % (D / 4));
+
+  auto load_tile = [&](const float* p, f32x4 (&x)[NT]) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[rt][r] = p[size_t(16 * rt + 4 * h4 + r) * D + col];
+  };
+  auto store_tile = [&](float* p, const f32x4 (&x)[NT]) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[size_t(16 * rt + 4 * h4 + r) * D + col] = x[rt][r];
+  };
+  // Chunk start states, as the states kernel stores them.
+  auto load_ws = [&](const float* p, f32x4 (&x)[NT]) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) x[rt] = ld4(p + (rt * NT + w) * 256 + 4 * lane);
+  };
 
   // ---- pass 2: chunks backwards ---------------------------------------------------
   f32x4 dS[NT];
@@ -756,6 +802,9 @@ hipError_t launch_prep(const ScanBwdArgs& a, hipStream_t stream) {
   const int64_t items = int64_t(a.n_chunks) * a.h_v;
   if (items <= 0) return hipSuccess;
   gdn_bwd_prep_kernel<D, F32IN><<<dim3(unsigned((items + 3) / 4)), dim3(256), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  gdn_bwd_states_kernel<D, F32IN><<<dim3(unsigned(a.n_seg * a.h_v)), dim3(4 * D), 0, stream>>>(a);
   return hipGetLastError();
 }
 

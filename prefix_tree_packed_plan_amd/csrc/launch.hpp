@@ -109,7 +109,7 @@ struct ScanBwdArgs {
   float* dg;             // [N, h_v]
   float* dbeta;          // [N, h_v]
   float* dinit;          // [n_roots, h_v, d, d] or null
-  float* hws;            // workspace: chunk start states [max_level_chunks, h_v, d, d]
+  float* hws;            // workspace: chunk start states [total_chunks, h_v, d, d]
   float* tws;            // workspace: chunk T, KK, QK [total_chunks, h_v, 3, 16, 16]
   float* dsseg;          // workspace: start-state gradients [n_seg, h_v, d, d]
   const int32_t* seg_off;
@@ -121,6 +121,7 @@ struct ScanBwdArgs {
   const int32_t* gchunk;
   const int32_t* chunk_seg;
   int32_t n_chunks;      // total chunks (prep launch)
+  int32_t n_seg;         // segments (states launch)
   const int32_t* items;  // segments of this level
   int32_t n_items;
   int32_t h_qk;
@@ -129,8 +130,9 @@ struct ScanBwdArgs {
   float scale;
 };
 
-// Scan backward (gdn_backward.hip); d = d_k = d_v.  The prep launch computes
-// every chunk's T, KK and QK (state-free); then one launch per trie level.
+// Scan backward (gdn_backward.hip); d = d_k = d_v.  The prep launches compute
+// every chunk's T, KK and QK (state-free) and every chunk's start state;
+// then one launch per trie level.
 hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream);
 hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream);
 // dst[t, j] = sum_m src[t, j group + m] over [n_tok, h_qk * group, d] fp32.

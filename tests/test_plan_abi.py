@@ -242,9 +242,9 @@ def test_schedule_constants_match_the_header():
 
 @pytest.mark.parametrize("cid", sorted(CONFIGS))
 def test_scan_backward_workspace_size_and_checks(cid):
-    """Workspace = chunk start states of the level with the most 16-token
-    chunks + [16, 16] T, KK, QK tiles of every chunk + one start-state
-    gradient per segment (+ per-value-head dq, dk
+    """Workspace = the start state and [16, 16] T, KK, QK tiles of every
+    16-token chunk + one start-state gradient per segment (+ per-value-head
+    dq, dk
     when value heads share a q/k head), fp32; undersized workspaces and bad
     arguments are rejected before any device work."""
     lib = _lib.load()
@@ -257,7 +257,7 @@ def test_scan_backward_workspace_size_and_checks(cid):
     chunks = [int(sum((lens[i] + 15) // 16 for i in range(len(parents)) if depth[i] == lv))
               for lv in range(int(depth.max()) + 1)]
     dd = s.d_k * s.d_v
-    want = (max(chunks) + len(parents)) * s.h_v * dd + sum(chunks) * s.h_v * 3 * 16 * 16  # + every chunk's T, KK, QK
+    want = (sum(chunks) + len(parents)) * s.h_v * dd + sum(chunks) * s.h_v * 3 * 16 * 16  # + every chunk's T, KK, QK
     if s.h_v != s.h_qk:
         want += 2 * int(lens.sum()) * s.h_v * s.d_k
     need = lib.tree_gdn_scan_backward_workspace_bytes(plan.handle, s.h_qk, s.h_v, s.d_k, s.d_v)
