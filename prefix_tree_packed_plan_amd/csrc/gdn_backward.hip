@@ -276,7 +276,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_states_kernel(ScanBwdArgs a)
   };
   auto store_ws = [&](float* p, const f32x4 (&x)[NT]) {
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) *reinterpret_cast<f32x4*>(p + (rt * NT + w) * 256 + 4 * lane) = x[rt];
+    for (int rt = 0; rt < NT; ++rt)
+      __builtin_nontemporal_store(x[rt], reinterpret_cast<f32x4*>(p + (rt * NT + w) * 256 + 4 * lane));
   };
 
   {
