@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 
 
 def scan_bwd_flops_per_token(s):
@@ -249,8 +250,12 @@ def main():
         fl = wl.n_tokens * scan_bwd_flops_per_token(s)
         bwd["tree_gdn_scan_backward"] = {
             "ms": sms, "unique_tokens_per_s": wl.n_tokens / sms * 1e3, "flops": fl, "TFLOP/s": fl / sms / 1e9,
-            "roofline": {"bound": "mfma", "dtype": "fp32", "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": fl / sms / 1e9 / FP32_MFMA_PEAK_TFLOPS},
+            # The dense products run on bf16 MFMA with fp32 operands split into
+            # hi + lo (two or three passes each); fp32-accurate results.
+            "roofline": {"bound": "mfma", "dtype": "bf16 (fp32 operands as hi + lo)",
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": fl / sms / 1e9 / BF16_MFMA_PEAK_TFLOPS,
+                         "frac_of_fp32_peak": fl / sms / 1e9 / FP32_MFMA_PEAK_TFLOPS},
             "workspace_GiB": sws.numel() / 2**30, "reps": reps}
         del states, do, sws
 
