@@ -347,7 +347,6 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.root_idx = base + p.m_root;
   a.kid_off = base + p.m_kid_off;
   a.kid = base + p.m_kid;
-  a.bchunk = base + p.m_bchunk;
   a.gchunk = base + p.m_gchunk;
   a.chunk_seg = base + p.m_chunk_seg;
   a.n_chunks = static_cast<int32_t>(p.total_chunks);

@@ -117,7 +117,6 @@ struct ScanBwdArgs {
   const int32_t* root_idx;
   const int32_t* kid_off;
   const int32_t* kid;
-  const int32_t* bchunk;
   const int32_t* gchunk;
   const int32_t* chunk_seg;
   int32_t n_chunks;      // total chunks (prep launch)

@@ -205,7 +205,7 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
     }
   }
 
-  // Scan backward: children lists and level-local chunk offsets.
+  // Scan backward: children lists and chunk offsets.
   p.kid_off.assign(n_seg + 1, 0);
   for (int32_t i = 0; i < n_seg; ++i)
     if (p.parents[i] >= 0) p.kid_off[p.parents[i] + 1] += 1;
@@ -215,16 +215,6 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
     std::vector<int32_t> fill(p.kid_off.begin(), p.kid_off.end() - 1);
     for (int32_t i = 0; i < n_seg; ++i)
       if (p.parents[i] >= 0) p.kid[fill[p.parents[i]]++] = i;
-  }
-  p.bchunk.assign(n_seg, 0);
-  for (int32_t l = 0; l < p.n_levels; ++l) {
-    int64_t c = 0;
-    for (int32_t j = p.level_start[l]; j < p.level_start[l + 1]; ++j) {
-      const int32_t s = p.order[j];
-      p.bchunk[s] = static_cast<int32_t>(c);
-      c += (p.lens[s] + Plan::kBwdChunk - 1) / Plan::kBwdChunk;
-    }
-    p.max_level_chunks = std::max(p.max_level_chunks, c);
   }
   p.gchunk.assign(n_seg, 0);
   for (int32_t i = 0; i < n_seg; ++i) {
@@ -251,8 +241,7 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   p.m_roots = p.m_fut + p.fut.size();
   p.m_kid_off = p.m_roots + p.roots.size();
   p.m_kid = p.m_kid_off + p.kid_off.size();
-  p.m_bchunk = p.m_kid + p.kid.size();
-  p.m_gchunk = p.m_bchunk + p.bchunk.size();
+  p.m_gchunk = p.m_kid + p.kid.size();
   p.m_chunk_seg = p.m_gchunk + p.gchunk.size();
   p.mirror.resize(p.m_chunk_seg + p.chunk_seg.size());
   std::copy(p.seg_off.begin(), p.seg_off.end(), p.mirror.begin() + p.m_seg_off);
@@ -271,7 +260,6 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   std::copy(p.roots.begin(), p.roots.end(), p.mirror.begin() + p.m_roots);
   std::copy(p.kid_off.begin(), p.kid_off.end(), p.mirror.begin() + p.m_kid_off);
   std::copy(p.kid.begin(), p.kid.end(), p.mirror.begin() + p.m_kid);
-  std::copy(p.bchunk.begin(), p.bchunk.end(), p.mirror.begin() + p.m_bchunk);
   std::copy(p.gchunk.begin(), p.gchunk.end(), p.mirror.begin() + p.m_gchunk);
   std::copy(p.chunk_seg.begin(), p.chunk_seg.end(), p.mirror.begin() + p.m_chunk_seg);
 

@@ -57,22 +57,19 @@ struct Plan {
 
   // Scan backward: kid[kid_off[s] .. kid_off[s+1]-1] are segment s's
   // children in index order (the fixed order in which their start-state
-  // gradients are summed into s's final-state gradient).  bchunk[s] is the
-  // offset of s's first kBwdChunk-token chunk among the chunks of its level
-  // (segments of a level in level order); max_level_chunks the largest
-  // level's chunk count (the chunk-state workspace is sized for it).
-  // gchunk[s] is the offset of s's first chunk among all chunks in segment
+  // gradients are summed into s's final-state gradient).  gchunk[s] is the
+  // offset of s's first kBwdChunk-token chunk among all chunks in segment
   // order, chunk_seg[c] the segment of chunk c (total_chunks of them).
   static constexpr int32_t kBwdChunk = 16;
-  std::vector<int32_t> kid_off, kid, bchunk, gchunk, chunk_seg;
-  int64_t max_level_chunks = 0, total_chunks = 0;
+  std::vector<int32_t> kid_off, kid, gchunk, chunk_seg;
+  int64_t total_chunks = 0;
 
   // Device copy: one int32 array; element offsets of each table inside it.
   std::vector<int32_t> mirror;
   size_t m_seg_off = 0, m_parent = 0, m_slot = 0, m_hist = 0, m_order = 0, m_root = 0, m_ctx = 0;
   size_t m_path_off = 0, m_path_seg = 0;
   size_t m_ent_off = 0, m_ent = 0, m_fut_off = 0, m_fut = 0, m_roots = 0;
-  size_t m_kid_off = 0, m_kid = 0, m_bchunk = 0, m_gchunk = 0, m_chunk_seg = 0;
+  size_t m_kid_off = 0, m_kid = 0, m_gchunk = 0, m_chunk_seg = 0;
 
   size_t device_bytes() const { return mirror.size() * sizeof(int32_t); }
 };
