@@ -1,5 +1,6 @@
 /*
- * tree_gdn.h -- C ABI of the tree conv + tree Gated DeltaNet library (forward and backward)
+ * tree_gdn.h -- C ABI of the tree conv + tree Gated DeltaNet library (forward and
+ * backward), with a tree Mamba2 (SSD) forward beside it,
  * for AMD Instinct MI355X (gfx950).
  *
  * The library runs the forward pass of a recurrent mixer over a prefix trie
@@ -347,6 +348,39 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
                            float* dinit_states, int64_t n_tokens, int32_t h_qk, int32_t h_v, int32_t d_k,
                            int32_t d_v, float scale, int32_t dtype, const tree_plan_t* plan, const void* dplan,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tree_ssd_scan -- Mamba2 (SSD) forward with the state forked over the trie
+ * (tree-recurrence 0.1.0 project page: "How a tree runs", a fork starts each
+ * segment from its parent's final state, and "Not yet", forking the Mamba2
+ * state; "Tree Training" section 3.1 Eq. 6, every token's result equals the
+ * standalone forward of its own root path).  Per head h, with group
+ * h / (n_heads / n_groups):
+ *     S_t = exp(dt_t A_h) S_{t-1} + dt_t B_t x_t^T,   y_t = S_t^T C_t + D_h x_t,
+ * S [d_state, head_dim] fp32; one launch per trie level, each segment
+ * starting from its parent's final state (a root from init_states or zero).
+ * x      device, [n_tokens, n_heads, head_dim], dtype      (read)
+ * dt     device, [n_tokens, n_heads] fp32, the step after softplus (>= 0)
+ *                                                          (read)
+ * A      device, [n_heads] fp32, the decay rate (< 0)      (read)
+ * B, C   device, [n_tokens, n_groups, d_state], dtype      (read)
+ * D      device, [n_heads] fp32, or NULL (no skip term)    (read)
+ * y      device, [n_tokens, n_heads, head_dim], dtype      (written)
+ * init_states device, [n_roots, n_heads, d_state, head_dim] fp32, or NULL
+ *                                                          (read)
+ * states device, [n_seg, n_heads, d_state, head_dim] fp32, or NULL: every
+ *        segment's final state (then the workspace may be empty)  (written)
+ * ws     device workspace of ws_bytes >= tree_scan_workspace_bytes(plan,
+ *        n_heads, d_state, head_dim, states != NULL).
+ * dtype  TREE_DTYPE_BF16 (bf16 MFMA; the products with the state take it as
+ *        hi + lo bf16) or TREE_DTYPE_F32 (fp32 MFMA).
+ * Compiled sizes: d_state in {64, 128}, head_dim in {32, 64}.
+ * Errors: INVALID_ARG, SIZE, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int tree_ssd_scan(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                  void* y, const float* init_states, float* states, int64_t n_tokens, int32_t n_groups,
+                  int32_t n_heads, int32_t d_state, int32_t head_dim, int32_t dtype, const tree_plan_t* plan,
+                  const void* dplan, void* ws, size_t ws_bytes, void* stream);
 
 /* Message for the last failed call on this thread ("" if none). */
 const char* tree_last_error(void);

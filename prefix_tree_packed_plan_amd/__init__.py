@@ -16,4 +16,5 @@ from ._lib import (  # noqa: F401
     tree_gdn_scan,
     tree_gdn_scan_backward,
     tree_plan,
+    tree_ssd_scan,
 )

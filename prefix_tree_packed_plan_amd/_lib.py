@@ -71,6 +71,8 @@ SIGNATURES = {
     "tree_gdn_scan_backward_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
     "tree_gdn_scan_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                               _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _SZ, _P]),
+    "tree_ssd_scan": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32,
+                                     _P, _P, _P, _SZ, _P]),
     "tree_last_error": (ctypes.c_char_p, []),
 }
 
@@ -423,3 +425,56 @@ def tree_gdn_scan_backward(q, k, v, g, beta, do, plan: TreePlan, states, scale: 
                                       plan.handle, dplan.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                       stream))
     return dq, dk, dv, dg, db, dinit
+
+
+def tree_ssd_scan(x, dt, A, B, C, plan: TreePlan, D=None, return_states: bool = False, out=None, states=None,
+                  workspace=None, init_states=None):
+    """Tree Mamba2 (SSD) forward: y [N, n_heads, head_dim] (and states
+    [n_seg, n_heads, d_state, head_dim] fp32).
+
+    x [N, n_heads, head_dim]; dt [N, n_heads] fp32 (after softplus); A
+    [n_heads] fp32 (< 0); B, C [N, n_groups, d_state] (x's dtype); D
+    [n_heads] fp32 or None; init_states [n_roots, n_heads, d_state,
+    head_dim] fp32 or None."""
+    import torch
+    _need(x, "x")
+    dev = x.device
+    f32 = torch.float32
+    _need(dt, "dt", f32, dev)
+    _need(A, "A", f32, dev)
+    _need(B, "B", x.dtype, dev)
+    _need(C, "C", x.dtype, dev)
+    if x.dim() != 3 or B.dim() != 3 or C.shape != B.shape or B.shape[0] != x.shape[0]:
+        raise ValueError("shapes must be x [N, H, P] and B, C [N, G, d_state]")
+    n, n_heads, head_dim = x.shape
+    n_groups, d_state = B.shape[1], B.shape[2]
+    if dt.shape != (n, n_heads) or A.shape != (n_heads,):
+        raise ValueError("dt must be [N, H] and A [H]")
+    if D is not None:
+        _need(D, "D", f32, dev)
+        if D.shape != (n_heads,):
+            raise ValueError("D must be [H]")
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", x.dtype, dev)
+    if return_states and states is None:
+        states = torch.empty((plan.n_seg, n_heads, d_state, head_dim), dtype=f32, device=dev)
+    if states is not None:
+        _need(states, "states", f32, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", f32, dev)
+        if tuple(init_states.shape) != (plan.n_roots, n_heads, d_state, head_dim):
+            raise ValueError("init_states must be [n_roots, H, d_state, P]")
+    lib = load()
+    need = int(lib.tree_scan_workspace_bytes(plan.handle, n_heads, d_state, head_dim, int(states is not None)))
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    dplan = plan.on_device(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    _check(lib.tree_ssd_scan(x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(), p(D),
+                             y.data_ptr(), p(init_states), p(states), n, n_groups, n_heads, d_state, head_dim,
+                             _dtype_code(x), plan.handle, dplan.data_ptr(), p(workspace),
+                             workspace.numel() if workspace is not None else 0, stream))
+    if return_states:
+        return y, states
+    return y

@@ -23,7 +23,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]
 # Packed fp32 instructions are kept out of the device code on purpose.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["plan.cpp", "api.cpp", "tree_conv.hip", "gdn_scan.hip", "gdn_scan_d128.hip", "gdn_backward.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "tree_conv.hip", "gdn_scan.hip", "gdn_scan_d128.hip", "gdn_backward.hip", "ssd_scan.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -375,6 +375,55 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   return TREE_OK;
 }
 
+int tree_ssd_scan(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                  void* y, const float* init_states, float* states, int64_t n_tokens, int32_t n_groups,
+                  int32_t n_heads, int32_t d_state, int32_t head_dim, int32_t dtype, const tree_plan_t* plan,
+                  const void* dplan, void* ws, size_t ws_bytes, void* stream) {
+  if (!plan || !x || !dt || !A || !B || !C || !y || !dplan)
+    return fail(TREE_ERR_INVALID_ARG, "tree_ssd_scan: null argument");
+  const tg::Plan& p = plan->p;
+  if (n_tokens != p.n_tokens)
+    return fail(TREE_ERR_SIZE, "tree_ssd_scan: n_tokens %lld != plan tokens %lld", static_cast<long long>(n_tokens),
+                static_cast<long long>(p.n_tokens));
+  if (n_groups <= 0 || n_heads <= 0 || d_state <= 0 || head_dim <= 0)
+    return fail(TREE_ERR_INVALID_ARG, "tree_ssd_scan: head counts and sizes must be > 0");
+  if (n_heads % n_groups != 0)
+    return fail(TREE_ERR_UNSUPPORTED, "tree_ssd_scan: n_heads %d is not a multiple of n_groups %d", n_heads, n_groups);
+  if (!dtype_ok(dtype)) return fail(TREE_ERR_INVALID_ARG, "tree_ssd_scan: bad dtype %d", dtype);
+  if (!tg::ssd_supported(d_state, head_dim, dtype))
+    return fail(TREE_ERR_UNSUPPORTED, "tree_ssd_scan: d_state=%d head_dim=%d dtype=%d not compiled in", d_state,
+                head_dim, dtype);
+  const size_t need = tree_scan_workspace_bytes(plan, n_heads, d_state, head_dim, states != nullptr);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(TREE_ERR_WORKSPACE, "tree_ssd_scan: workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0, need);
+  const int32_t* base = static_cast<const int32_t*>(dplan);
+  tg::SsdArgs a{};
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.y = y;
+  a.init = init_states;
+  a.states = states;
+  a.slots = static_cast<float*>(ws);
+  a.seg_off = base + p.m_seg_off;
+  a.parent = base + p.m_parent;
+  a.slot = base + p.m_slot;
+  a.root_idx = base + p.m_root;
+  a.n_groups = n_groups;
+  a.n_heads = n_heads;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int32_t l = 0; l < p.n_levels; ++l) {
+    a.items = base + p.m_order + p.level_start[l];
+    a.n_items = p.level_start[l + 1] - p.level_start[l];
+    const hipError_t e = tg::launch_ssd_scan(a, d_state, head_dim, dtype, st);
+    if (e != hipSuccess) return hip_fail("tree_ssd_scan: launch", e);
+  }
+  return TREE_OK;
+}
+
 const char* tree_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"

@@ -1,0 +1,146 @@
+// Chunk-level MFMA helpers shared by the scan backward and the Mamba2 (SSD)
+// scan (gfx950): fp32 16x16x4 products, split-bf16 16x16x32 / 16x16x16
+// products, 16-lane reductions and the per-lane gate values of a 16-token
+// chunk.
+//
+// Accumulator layout: lane l = 16 h + i (h = l / 16) holds rows 4h + r,
+// column i of a 16x16 tile.  A 16-deep fp32 contraction is four
+// v_mfma_f32_16x16x4_f32; in step s lane l supplies contraction index 4h + s,
+// so an accumulator tile is the B operand of a product that contracts its
+// rows, and the accumulator tile of X^T is the A operand of X times a matrix.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace tg {
+namespace chunk {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int L = 16;  // chunk length (tokens)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// c + A B over a 16-deep contraction: a[s] = A[i][4h + s], b[s] = B[4h + s][i].
+__device__ __forceinline__ f32x4 mm(const f32x4 a, const f32x4 b, f32x4 c) {
+  c = mfma(a[0], b[0], c);
+  c = mfma(a[1], b[1], c);
+  c = mfma(a[2], b[2], c);
+  return mfma(a[3], b[3], c);
+}
+__device__ __forceinline__ f32x4 z4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- split-bf16 products (bf16 inputs) ------------------------------------------
+// An fp32 operand x is carried as hi + lo bf16 (x - hi - lo within 2^-18 |x|);
+// q, k and dO are exact in bf16.  A product of an exact operand with a split
+// one takes two MFMAs (hi, lo); of two split ones three (lo x lo dropped).
+// 16x16x32 operands: lane l supplies contraction indices kmap(h, e) =
+// e < 4 ? 4h + e : 16 + 4h + (e - 4), the same permutation on both sides, so
+// two accumulator row tiles (rows 4h + r and 16 + 4h + r) form one B operand.
+
+// Two floats -> two bf16 (round to nearest even), `a` in the low half.
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint2 pack4(const f32x4 x) { return make_uint2(pk2(x[0], x[1]), pk2(x[2], x[3])); }
+__device__ __forceinline__ void split4(const f32x4 x, uint2& hi, uint2& lo) {
+  const uint32_t h0 = pk2(x[0], x[1]), h1 = pk2(x[2], x[3]);
+  hi = make_uint2(h0, h1);
+  lo = make_uint2(pk2(x[0] - lo_f(h0), x[1] - hi_f(h0)), pk2(x[2] - lo_f(h1), x[3] - hi_f(h1)));
+}
+__device__ __forceinline__ uint4 cat(const uint2 a, const uint2 b) { return make_uint4(a.x, a.y, b.x, b.y); }
+// hi and lo of the 8 values (x0 = kmap entries 0..3, x1 = entries 4..7).
+__device__ __forceinline__ void split8(const f32x4 x0, const f32x4 x1, uint4& hi, uint4& lo) {
+  uint2 h0, l0, h1, l1;
+  split4(x0, h0, l0);
+  split4(x1, h1, l1);
+  hi = cat(h0, h1);
+  lo = cat(l0, l1);
+}
+__device__ __forceinline__ f32x4 mma32(const uint4 a, const uint4 b, const f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16b(const uint2 a, const uint2 b, const f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                   0, 0, 0);
+}
+// Exact (bf16-valued) A operand of a 32-deep contraction from an fp32 LDS row:
+// p points at column 4h of the block.
+__device__ __forceinline__ uint4 exact8(const float* p) { return cat(pack4(ld4(p)), pack4(ld4(p + 16))); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of a row (lanes 16h .. 16h+15); every lane gets it.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
+// Per-lane gate values of one chunk.
+struct Gates {
+  f32x4 gam, del, bet;  // gamma, delta, beta at rows 4h + r
+  f32x4 Gm, Gmt;        // Gamma at (row, col) and at (col, row), zero where masked
+  float gam_c, del_c, bet_c, gam_last;  // at column i, and gamma_last
+};
+
+__device__ __forceinline__ Gates make_gates(const float* g, const float* b, int h4, int i16) {
+  float grow[4] = {0.f, 0.f, 0.f, 0.f}, gcol = 0.f, run = 0.f;
+#pragma unroll
+  for (int t = 0; t < L; ++t) {
+    run += g[t];  // the same running sum in every lane: G is bitwise consistent
+#pragma unroll
+    for (int r = 0; r < 4; ++r) grow[r] = (t == 4 * h4 + r) ? run : grow[r];
+    gcol = (t == i16) ? run : gcol;
+  }
+  const float glast = run * kLog2e, gc = gcol * kLog2e;
+  Gates s;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * h4 + r;
+    const float gr = grow[r] * kLog2e;
+    s.gam[r] = ex2(gr);
+    s.del[r] = ex2(glast - gr);
+    s.bet[r] = b[row];
+    s.Gm[r] = row >= i16 ? ex2(gr - gc) : 0.f;
+    s.Gmt[r] = i16 >= row ? ex2(gc - gr) : 0.f;
+  }
+  s.gam_c = ex2(gc);
+  s.del_c = ex2(glast - gc);
+  s.bet_c = b[i16];
+  s.gam_last = ex2(glast);
+  return s;
+}
+
+template <bool F32IN>
+__device__ __forceinline__ f32x4 load4(const void* base, size_t idx) {
+  if (F32IN) return ld4(static_cast<const float*>(base) + idx);
+  const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xffff0000u)};
+}
+template <bool F32IN>
+__device__ __forceinline__ float load1(const void* base, size_t idx) {
+  if (F32IN) return static_cast<const float*>(base)[idx];
+  return __uint_as_float(uint32_t(static_cast<const uint16_t*>(base)[idx]) << 16);
+}
+
+}  // namespace chunk
+}  // namespace tg

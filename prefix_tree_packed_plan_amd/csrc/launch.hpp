@@ -139,4 +139,29 @@ hipError_t launch_head_group_sum(const float* src, float* dst, int64_t n_tok, in
                                  hipStream_t stream);
 bool scan_backward_supported(int d_k, int d_v, int dtype);
 
+struct SsdArgs {
+  const void* x;       // [N, n_heads, head_dim]
+  const float* dt;     // [N, n_heads], after softplus
+  const float* A;      // [n_heads], < 0
+  const void* B;       // [N, n_groups, d_state]
+  const void* C;       // [N, n_groups, d_state]
+  const float* D;      // [n_heads] or null
+  void* y;             // [N, n_heads, head_dim]
+  const float* init;   // [n_roots, n_heads, d_state, head_dim] or null (zeros)
+  float* states;       // [n_seg, n_heads, d_state, head_dim] or null
+  float* slots;        // [n_parents, n_heads, d_state, head_dim] when states is null
+  const int32_t* seg_off;
+  const int32_t* parent;
+  const int32_t* slot;
+  const int32_t* root_idx;
+  const int32_t* items;  // segments of this level
+  int32_t n_items;
+  int32_t n_groups;
+  int32_t n_heads;
+};
+
+// Mamba2 (SSD) forward over one trie level (ssd_scan.hip).
+hipError_t launch_ssd_scan(const SsdArgs& a, int d_state, int head_dim, int dtype, hipStream_t stream);
+bool ssd_supported(int d_state, int head_dim, int dtype);
+
 }  // namespace tg

@@ -2,8 +2,8 @@
 
 This package is shared by the oracle tests, the GPU tests and the benchmark.
 It only draws random numbers and shapes them into the layouts the tree
-conv and tree Gated DeltaNet scan consume; it performs none of the method's
-arithmetic.
+conv, the tree Gated DeltaNet scan and the tree Mamba2 (SSD) scan consume;
+it performs none of the method's arithmetic.
 """
 from .gen import (  # noqa: F401
     CONFIGS,
@@ -12,5 +12,7 @@ from .gen import (  # noqa: F401
     make_trie,
     make_conv_inputs,
     make_scan_inputs,
+    make_ssd_inputs,
+    SSD_SHAPE,
     make_workload,
 )

@@ -30,7 +30,8 @@ from typing import Dict, Optional
 import numpy as np
 
 # Tensor ids for the per-tensor generators.
-_TID = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "x": 6, "w": 7, "bias": 8}
+_TID = {"q": 1, "k": 2, "v": 3, "g": 4, "beta": 5, "x": 6, "w": 7, "bias": 8,
+        "ssd_x": 9, "ssd_dt": 10, "ssd_A": 11, "ssd_B": 12, "ssd_C": 13}
 
 
 @dataclass(frozen=True)
@@ -186,6 +187,31 @@ def make_conv_inputs(n_tokens, channels, width, dtype, device="cpu", seed=0,
     if with_bias:
         out["bias"] = _randn((channels,), device, seed, "bias", std=0.5).to(td).contiguous()
     return out
+
+
+# Mamba2-2.7B-shaped heads for the tree Mamba2 (SSD) scan: 80 heads of 64,
+# d_state 128, one B/C group.
+SSD_SHAPE = {"n_groups": 1, "n_heads": 80, "d_state": 128, "head_dim": 64}
+
+
+def make_ssd_inputs(n_tokens, n_groups, n_heads, d_state, head_dim, dtype, device="cpu", seed=0):
+    """Mamba2 (SSD) inputs at the ranges of Mamba2's initialisation: x, B, C
+    ~ N(0, 1) in `dtype` (x [N,H,P], B and C [N,G,d_state]); dt [N,H] fp32
+    log-uniform on [0.001, 0.1] (a step after softplus); A [H] fp32 =
+    -exp(U[log 1, log 16]); D [H] fp32 = 1."""
+    torch = _torch()
+    td = _tdtype(dtype)
+    u_dt = torch.rand((n_tokens, n_heads), generator=_gen(device, seed, "ssd_dt"), device=device)
+    u_a = torch.rand((n_heads,), generator=_gen(device, seed, "ssd_A"), device=device)
+    lo, hi = float(np.log(1e-3)), float(np.log(1e-1))
+    return {
+        "x": _randn((n_tokens, n_heads, head_dim), device, seed, "ssd_x").to(td).contiguous(),
+        "dt": torch.exp(lo + (hi - lo) * u_dt).contiguous(),
+        "A": (-torch.exp(u_a * float(np.log(16.0)))).contiguous(),
+        "B": _randn((n_tokens, n_groups, d_state), device, seed, "ssd_B").to(td).contiguous(),
+        "C": _randn((n_tokens, n_groups, d_state), device, seed, "ssd_C").to(td).contiguous(),
+        "D": torch.ones((n_heads,), device=device, dtype=torch.float32),
+    }
 
 
 @dataclass
