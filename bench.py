@@ -132,6 +132,7 @@ def main():
     ap.add_argument("--no-rescan-compare", action="store_true",
                     help="skip the untimed-by-the-step comparison run of the rescan schedule")
     ap.add_argument("--no-backward", action="store_true", help="skip the separately timed conv and scan backward")
+    ap.add_argument("--no-ssd", action="store_true", help="skip the separately timed tree Mamba2 (SSD) scan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="before timing, run one plain 1 GiB device copy (a counter reference for profiles)")
@@ -259,6 +260,38 @@ def main():
             "workspace_GiB": sws.numel() / 2**30, "reps": reps}
         del states, do, sws
 
+    # The tree Mamba2 (SSD) scan on the same trie, Mamba2-2.7B-shaped heads
+    # (timed on its own, outside the step).
+    ssd = None
+    if not args.no_ssd:
+        from workloads import SSD_SHAPE, make_ssd_inputs
+        sh = SSD_SHAPE
+        si = make_ssd_inputs(wl.n_tokens, sh["n_groups"], sh["n_heads"], sh["d_state"], sh["head_dim"], "bf16", dev)
+        yb = torch.empty_like(si["x"])
+        ssws = torch.empty(max(int(lib.tree_scan_workspace_bytes(plan.handle, sh["n_heads"], sh["d_state"],
+                                                                  sh["head_dim"], 0)), 1), dtype=torch.uint8, device=dev)
+        sargs = (si["x"], si["dt"], si["A"], si["B"], si["C"], plan)
+        for _ in range(2):
+            ptp.tree_ssd_scan(*sargs, D=si["D"], out=yb, workspace=ssws)
+        reps = max(3, min(args.steps, 10))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            ptp.tree_ssd_scan(*sargs, D=si["D"], out=yb, workspace=ssws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        yms = ev[0].elapsed_time(ev[1]) / reps
+        # x, y (H * P bf16 each), B, C (G * d_state bf16 each), dt (H fp32) per
+        # token, plus one write and one read of each parent's state.
+        per_tok = 2 * sh["n_heads"] * sh["head_dim"] * 2 + 2 * sh["n_groups"] * sh["d_state"] * 2 + sh["n_heads"] * 4
+        sb = wl.n_tokens * per_tok + 2 * st["n_parents"] * sh["n_heads"] * sh["d_state"] * sh["head_dim"] * 4
+        ssd = {"tree_ssd_scan": {
+            "ms": yms, "unique_tokens_per_s": wl.n_tokens / yms * 1e3, "bytes": sb, "GB/s": sb / yms / 1e6,
+            "roofline": {"bound": "hbm", "achieved": sb / yms / 1e6, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": sb / (HBM_PEAK_GBS * 1e9) / (yms * 1e-3)},
+            "shape": dict(sh, dtype="bf16"), "launches": st["n_levels"], "reps": reps}}
+        del si, yb, ssws
+
     n = wl.n_tokens
     state_bytes = 2 * st["n_parents"] * s.h_v * s.d_k * s.d_v * 4  # write + read once
     conv_b = n * conv_bytes_per_token(s)
@@ -312,6 +345,8 @@ def main():
     }
     if bwd is not None:
         out["backward"] = bwd
+    if ssd is not None:
+        out["ssd"] = ssd
     if other is not None:
         fork_ms = scan_ms if sched == "level" else other["scan_ms"]
         rescan_ms = other["scan_ms"] if sched == "level" else scan_ms

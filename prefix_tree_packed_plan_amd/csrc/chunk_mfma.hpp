@@ -102,20 +102,22 @@ struct Gates {
 };
 
 __device__ __forceinline__ Gates make_gates(const float* g, const float* b, int h4, int i16) {
-  float grow[4] = {0.f, 0.f, 0.f, 0.f}, gcol = 0.f, run = 0.f;
-#pragma unroll
-  for (int t = 0; t < L; ++t) {
-    run += g[t];  // the same running sum in every lane: G is bitwise consistent
-#pragma unroll
-    for (int r = 0; r < 4; ++r) grow[r] = (t == 4 * h4 + r) ? run : grow[r];
-    gcol = (t == i16) ? run : gcol;
-  }
-  const float glast = run * kLog2e, gc = gcol * kLog2e;
+  // G = inclusive prefix sum of g over the chunk: a scan across the 16 lanes
+  // of each row (lane i ends with G_i), then the lane's rows 4h + r and the
+  // last token read from the lanes that hold them.  Row and column values
+  // come from the same G, so Gamma_ii = 1 exactly.
+  float G = g[i16];
+  G += dpp<0x111>(G);  // row_shr:1
+  G += dpp<0x112>(G);  // row_shr:2
+  G += dpp<0x114>(G);  // row_shr:4
+  G += dpp<0x118>(G);  // row_shr:8
+  const int base = 16 * h4;
+  const float glast = __shfl(G, base + 15, 64) * kLog2e, gc = G * kLog2e;
   Gates s;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * h4 + r;
-    const float gr = grow[r] * kLog2e;
+    const float gr = __shfl(G, base + row, 64) * kLog2e;
     s.gam[r] = ex2(gr);
     s.del[r] = ex2(glast - gr);
     s.bet[r] = b[row];
