@@ -277,3 +277,28 @@ def test_scan_backward_workspace_size_and_checks(cid):
     assert call(h_qk=3, h_v=4) == -4
     assert call(dtype=7) == -1
     assert call(states=None) == -1
+
+
+def test_ssd_scan_argument_checks_need_no_device():
+    """tree_ssd_scan validates sizes, head/group counts, dtype, compiled sizes
+    and the workspace before any device work."""
+    lib = _lib.load()
+    parents, lens, _ = make_trie(2)
+    plan = _lib.TreePlan(parents, lens, 4)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    n = plan.n_tokens
+    need = lib.tree_scan_workspace_bytes(plan.handle, 8, 128, 64, 0)
+    assert need == 1 * 8 * 128 * 64 * 4  # one parent state slot per head
+
+    def call(n_tok=n, groups=1, heads=8, d_state=128, head_dim=64, dtype=1, ws=need, states=None, x=fake):
+        return lib.tree_ssd_scan(x, fake, fake, fake, fake, None, fake, None, states, n_tok, groups, heads, d_state,
+                                 head_dim, dtype, plan.handle, fake, fake, ws, None)
+
+    assert call(n_tok=n - 1) == -3
+    assert call(groups=3) == -4
+    assert call(d_state=96) == -4
+    assert call(head_dim=128) == -4
+    assert call(dtype=5) == -1
+    assert call(ws=need - 1) == -5
+    assert call(x=None) == -1
+    assert b"tree_ssd_scan" in lib.tree_last_error()
