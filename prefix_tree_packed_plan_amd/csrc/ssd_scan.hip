@@ -36,13 +36,14 @@ namespace {
 
 using namespace chunk;
 
-template <int N>
+template <int N, int P>
 struct SsdSmem {
   static constexpr int S = N + 4;  // row stride (floats)
   alignas(16) float g[L];   // dt A
   alignas(16) float b[L];   // dt
   alignas(16) float bm[L * S];  // B rows
   alignas(16) float cm[L * S];  // C rows
+  alignas(16) float y[L * P];   // the chunk's outputs, stored as whole rows after the chunk
 };
 
 template <int N, int P, bool F32IN>
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(4 * P, 2) void ssd_level_kernel(SsdArgs a) {
   constexpr int NT = N / 16;  // row tiles of the state
   constexpr int NTH = 4 * P;  // threads
   constexpr int S = N + 4;
-  __shared__ SsdSmem<N> sm;
+  __shared__ SsdSmem<N, P> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,16 +138,7 @@ __global__ __launch_bounds__(4 * P, 2) void ssd_level_kernel(SsdArgs a) {
     }
     const f32x4 Y = mm(Pt, U, gt.gam * cs) + Dh * xv;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * h4 + r;
-      if (row < n) {
-        const size_t oi = (size_t(t0 + row) * a.n_heads + h) * P + col;
-        if constexpr (F32IN)
-          static_cast<float*>(a.y)[oi] = Y[r];
-        else
-          static_cast<uint16_t*>(a.y)[oi] = static_cast<uint16_t>(pk2(Y[r], 0.f) & 0xffffu);
-      }
-    }
+    for (int r = 0; r < 4; ++r) sm.y[(4 * h4 + r) * P + col] = Y[r];
     // -- S = gamma_last S + B^T diag(delta) U
     const f32x4 dU = gt.del * U;
     uint2 uh, ul;
@@ -163,7 +155,25 @@ __global__ __launch_bounds__(4 * P, 2) void ssd_level_kernel(SsdArgs a) {
         St[rt] = mma16b(ab, ul, mma16b(ab, uh, gt.gam_last * St[rt]));
       }
     }
-    __syncthreads();  // the chunk's tables are read
+    __syncthreads();  // the chunk's tables are read and its outputs staged
+    // -- store the chunk's rows of y: a (token, head) row is P contiguous
+    //    values, written by consecutive threads with 16-byte stores
+    {
+      constexpr int EPS = F32IN ? 4 : 8;  // elements per 16-byte store
+      constexpr int PER_ROW = P / EPS;
+      for (int e = tid; e < L * PER_ROW; e += NTH) {
+        const int row = e / PER_ROW, c0 = EPS * (e % PER_ROW);
+        if (row >= n) continue;
+        const float* src = &sm.y[row * P + c0];
+        const size_t oi = (size_t(t0 + row) * a.n_heads + h) * P + c0;
+        if constexpr (F32IN) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.y) + oi) = ld4(src);
+        } else {
+          const uint4 v = cat(pack4(ld4(src)), pack4(ld4(src + 4)));
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + oi) = v;
+        }
+      }
+    }
   }
 
   float* dst = a.states ? a.states + (size_t(seg) * a.n_heads + h) * hs
