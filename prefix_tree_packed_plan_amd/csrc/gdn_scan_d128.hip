@@ -34,6 +34,8 @@
 //
 // Products that feed the state carry their fp32 operand as hi + lo bf16
 // (relative 2^-17; lo x lo dropped); the output path uses hi only.  The
+// state's own split takes its exact residual S - hi from an MFMA (split4m),
+// which leaves the vector ALU two conversions per pair of values.  The
 // output is produced transposed, so a lane holds 4 consecutive value columns
 // of one token.
 //
@@ -116,6 +118,25 @@ __device__ __forceinline__ f32x4 mma16x3(const uint2 ah, const uint2 al, const u
   return mma16(al, bh, c);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// x = hi + lo as split4, with the residual lo = x - float(hi) formed by a
+// 16x16x16 MFMA instead of the vector ALU: -I times the packed hi (exact
+// products) added to x, which enters as the fp32 accumulator input.  The sum
+// is exactly representable, so lo is bitwise the same as split4's; the vector
+// ALU only does the two conversions.  x is one accumulator tile (lane (n, h)
+// holds rows 4h..4h+3 of column n), which is also the B operand layout of hi;
+// negI is the A operand of -I (lane (m, h): -1 at column m of 4h..4h+3).
+__device__ __forceinline__ void split4m(const f32x4 x, const uint2 negI, uint2& hi, uint2& lo) {
+  hi = make_uint2(pk2(x[0], x[1]), pk2(x[2], x[3]));
+  const f32x4 r = mma16(negI, hi, x);
+  lo = make_uint2(pk2(r[0], r[1]), pk2(r[2], r[3]));
+}
+__device__ __forceinline__ void split8m(const f32x4 x0, const f32x4 x1, const uint2 negI, uint4& hi, uint4& lo) {
+  uint2 h0, l0, h1, l1;
+  split4m(x0, negI, h0, l0);
+  split4m(x1, negI, h1, l1);
+  hi = make_uint4(h0.x, h0.y, h1.x, h1.y);
+  lo = make_uint4(l0.x, l0.y, l1.x, l1.y);
+}
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Lane i gets lane i - n of its row of 16 (0 for the first n lanes of a row).
 __device__ __forceinline__ float dpp_shr(float x, int n) {
@@ -225,6 +246,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h4 = lane >> 4;
   const int i16 = lane & 15;
+  // -I as a 16x16x16 A operand (split4m).
+  uint2 negI;
+  {
+    const int j = i16 - 4 * h4;
+    negI = make_uint2((j == 0 ? 0xBF80u : 0u) | (j == 1 ? 0xBF800000u : 0u),
+                      (j == 2 ? 0xBF80u : 0u) | (j == 3 ? 0xBF800000u : 0u));
+  }
 
   // Block -> (item, value head).  When value heads come in pairs per q/k head
   // and h_v is a multiple of 16, the pair lands on blocks b and b + 8, which
@@ -503,7 +531,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint4 sh, sl;
-      split8(S[2 * kk], S[2 * kk + 1], sh, sl);
+      split8m(S[2 * kk], S[2 * kk + 1], negI, sh, sl);
       S[2 * kk] *= gL;
       S[2 * kk + 1] *= gL;
 #pragma unroll
