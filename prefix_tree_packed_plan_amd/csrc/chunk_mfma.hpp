@@ -81,6 +81,70 @@ __device__ __forceinline__ f32x4 mma16b(const uint2 a, const uint2 b, const f32x
 // p points at column 4h of the block.
 __device__ __forceinline__ uint4 exact8(const float* p) { return cat(pack4(ld4(p)), pack4(ld4(p + 16))); }
 
+// x = hi + lo as split4, with the exact residual x - float(hi) from a
+// 16x16x16 MFMA: -I times the packed hi (exact products) added to x as the
+// fp32 accumulator input.  The sum is exactly representable, so lo is bitwise
+// split4's, and the vector ALU does only the two conversions.  x is one
+// accumulator tile, which is also the B operand layout of hi; negI is the A
+// operand of -I (neg_identity()).
+__device__ __forceinline__ uint2 neg_identity(int h4, int i16) {
+  const int j = i16 - 4 * h4;
+  return make_uint2((j == 0 ? 0xBF80u : 0u) | (j == 1 ? 0xBF800000u : 0u),
+                    (j == 2 ? 0xBF80u : 0u) | (j == 3 ? 0xBF800000u : 0u));
+}
+__device__ __forceinline__ void split4m(const f32x4 x, const uint2 negI, uint2& hi, uint2& lo) {
+  hi = pack4(x);
+  lo = pack4(mma16b(negI, hi, x));
+}
+__device__ __forceinline__ void split8m(const f32x4 x0, const f32x4 x1, const uint2 negI, uint4& hi, uint4& lo) {
+  uint2 h0, l0, h1, l1;
+  split4m(x0, negI, h0, l0);
+  split4m(x1, negI, h1, l1);
+  hi = cat(h0, h1);
+  lo = cat(l0, l1);
+}
+
+// ---- bf16 tiles of 256-byte rows in LDS (d = 128) --------------------------------
+// Rows in 4-row blocks of 1 KB (the 64 lanes x 16 bytes of one LDS DMA) at an
+// 1088-byte stride, block b shifted by a further {0, 2, 1, 3}[b % 4] x 16
+// bytes, and the 16-byte chunk c of row r at slot c ^ 4(r % 4): MFMA operand
+// reads (two 8-byte pieces 32 bytes apart, 16 rows) and transposing reads
+// (4 rows x 16 columns) then hit every LDS bank once per half-wave.
+constexpr int kTileRow16 = 4352;  // bytes of 16 rows
+__device__ __forceinline__ int tile_blk(int b) { return b * 1088 + 16 * ((0x3120 >> (4 * (b & 3))) & 3); }
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return tile_blk(row >> 2) + (row & 3) * 256 + 16 * ((col >> 3) ^ (4 * (row & 3))) + 2 * (col & 7);
+}
+// The global 16-byte chunk that lane `ln` of a block DMA loads, so that it
+// lands at its swizzled slot (row ln / 16 of the block, slot ln % 16).
+__device__ __forceinline__ int tile_dma_chunk(int ln) { return (ln & 15) ^ (4 * (ln >> 4)); }
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2 lds_cu2;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+// 16x16x32 operand (A or B) of row `row` at byte offset o = tile_off(row,
+// 32m + 4h): columns 32m + kmap(h, 0..7).  o2 is o + 32, passed as a
+// separate register so that the two 8-byte reads are not fused into one
+// ds_read2_b64 (several times slower on this part).
+__device__ __forceinline__ uint4 tile_a8(const char* t, int o, int o2) {
+  const u32x2 x = *(lds_cu2*)(t + o), y = *(lds_cu2*)(t + o2);
+  return make_uint4(x[0], x[1], y[0], y[1]);
+}
+// Transposing read: lane i of 16-lane group h passes the address of (row0 +
+// 4h + i / 4, col0 + 4 (i % 4)) and gets rows row0 + 4h + 0..3 of column
+// col0 + i (4 bf16), i.e. the accumulator / 16x16x16 operand layout.
+__device__ __forceinline__ uint2 tile_tr(const char* t, int o) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + o)));
+}
+__device__ __forceinline__ f32x4 bf4(const uint2 w) {
+  return f32x4{lo_f(w.x), hi_f(w.x), lo_f(w.y), hi_f(w.y)};
+}
+// Buffer descriptor over `bytes` bytes from `base` (raw, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, static_cast<int>(bytes), 0x00020000);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));

@@ -186,10 +186,225 @@ __global__ __launch_bounds__(4 * P, 2) void ssd_level_kernel(SsdArgs a) {
   }
 }
 
+// ---- bf16, d_state = 128 -----------------------------------------------------------
+// The same algebra with the chunk's inputs moved by DMA: B and C rows (256
+// bytes each) land in swizzled bf16 tiles, x rows in a row-major tile and dt
+// in a row of floats, all written to LDS by buffer loads straight from HBM,
+// one chunk ahead into the other half of double buffers.  MFMA operands are
+// read from the tiles as they are (C and B rows for C S0 and C B^T; B^T and x
+// by transposing reads), the state's hi/lo split takes its residual from an
+// MFMA, and the outputs are staged as bf16 and stored as whole rows during the
+// next chunk.
+template <int P>
+struct SsdTileSmem {
+  alignas(16) char bt[2][kTileRow16];  // B rows of the chunk
+  alignas(16) char ct[2][kTileRow16];  // C rows
+  alignas(16) char xt[2][L * P * 2];   // x rows (row-major, 2P bytes each)
+  alignas(16) float dt[2][L];
+  alignas(16) uint16_t ys[2][L * P];   // staged outputs (bf16, row-major)
+};
+
+template <int P>
+__global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) void ssd_bf16_n128_kernel(SsdArgs a) {
+  constexpr int N = 128;
+  constexpr int NT = N / 16;  // row tiles of the state
+  constexpr int NW = P / 16;  // waves
+  constexpr int XB = L * P * 2 / 1024;  // 1 KB DMA blocks of the x tile
+  __shared__ SsdTileSmem<P> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h4 = lane >> 4;
+  const int i16 = lane & 15;
+  const int col = 16 * w + i16;
+  const uint2 negI = neg_identity(h4, i16);
+
+  const int item = blockIdx.x / a.n_heads;
+  const int h = blockIdx.x - item * a.n_heads;
+  const int seg = a.items[item];
+  const int grp = h / (a.n_heads / a.n_groups);
+  const int par = a.parent[seg];
+  const size_t hs = size_t(N) * P;
+  const float Ah = a.A[h];
+  const float Dh = a.D ? a.D[h] : 0.f;
+  const uint16_t* Bg = static_cast<const uint16_t*>(a.B);
+  const uint16_t* Cg = static_cast<const uint16_t*>(a.C);
+  const uint16_t* xg = static_cast<const uint16_t*>(a.x);
+  uint16_t* yg = static_cast<uint16_t*>(a.y);
+  const int rs_bc = a.n_groups * N * 2, rs_x = a.n_heads * P * 2;  // bytes between token rows
+
+  // Loop-constant LDS offsets: operand reads of row i16 at columns 32m + 4h4
+  // (o2 = o + 32, opaque); transposing reads of B at columns 16rt and of x at
+  // this wave's columns.
+  int ao[NT / 2], ao2[NT / 2];
+#pragma unroll
+  for (int m = 0; m < NT / 2; ++m) {
+    ao[m] = tile_off(i16, 32 * m + 4 * h4);
+    ao2[m] = ao[m] + 32;
+    asm volatile("" : "+v"(ao2[m]));
+  }
+  // B^T rows 16rt.. at bo[rt / 2] + 32 (rt % 2): the swizzle keeps a 16-column
+  // step inside a 32-column block a plain 32-byte step, but not across blocks.
+  int bo[NT / 2];
+#pragma unroll
+  for (int m = 0; m < NT / 2; ++m) bo[m] = tile_off(4 * h4 + (i16 >> 2), 32 * m + 4 * (i16 & 3));
+  const int xo = (4 * h4 + (i16 >> 2)) * (2 * P) + 2 * (16 * w + 4 * (i16 & 3));
+
+  f32x4 St[NT];
+  {
+    const float* src = nullptr;
+    if (par >= 0)
+      src = a.states ? a.states + (size_t(par) * a.n_heads + h) * hs
+                     : a.slots + (size_t(a.slot[par]) * a.n_heads + h) * hs;
+    else if (a.init)
+      src = a.init + (size_t(a.root_idx[seg]) * a.n_heads + h) * hs;
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) St[rt][r] = src ? src[size_t(16 * rt + 4 * h4 + r) * P + col] : 0.f;
+  }
+
+  // Chunk at token tc (rows past the segment end repeat its last row; their
+  // dt is taken as zero below) into buffer buf.  Wave w loads B and C row
+  // blocks w, w + NW, ...; the first waves the x blocks; the last wave dt.
+  auto fetch = [&](int tc, int end, int buf) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int Ln = min(L, end - tc);
+    const auto rb = rsrc(Bg + (size_t(tc) * a.n_groups + grp) * N, L * rs_bc);
+    const auto rc = rsrc(Cg + (size_t(tc) * a.n_groups + grp) * N, L * rs_bc);
+    const int cofs = 16 * tile_dma_chunk(ln);
+#pragma unroll
+    for (int blk = w; blk < 4; blk += NW) {
+      const int ob = min(4 * blk + (ln >> 4), Ln - 1) * rs_bc + cofs;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sm.bt[buf] + tile_blk(blk)), 16, ob, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(sm.ct[buf] + tile_blk(blk)), 16, ob, 0, 0, 0);
+    }
+    if (w < XB) {  // rows of 2P bytes, 1024 / (2P) rows per block
+      constexpr int RPB = 1024 / (2 * P), CPR = 2 * P / 16;
+      const auto rx = rsrc(xg + (size_t(tc) * a.n_heads + h) * P, L * rs_x);
+      const int ox = min(RPB * w + ln / CPR, Ln - 1) * rs_x + 16 * (ln % CPR);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sm.xt[buf] + 1024 * w), 16, ox, 0, 0, 0);
+    }
+    if (w == NW - 1 && lane < L) {
+      const auto rd = rsrc(a.dt + size_t(tc) * a.n_heads + h, L * a.n_heads * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)sm.dt[buf], 4, min(lane, Ln - 1) * a.n_heads * 4, 0,
+                                               0, 0);
+    }
+  };
+  // Whole rows of the staged outputs of the chunk at tc (n rows).
+  auto store_y = [&](int tc, int n, int buf) {
+    constexpr int CPR = 2 * P / 16;  // 16-byte chunks per row
+    for (int e = tid; e < L * CPR; e += 4 * P) {
+      const int row = e / CPR, c = e % CPR;
+      if (row < n) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&sm.ys[buf][row * P + 8 * c]);
+        *reinterpret_cast<uint4*>(yg + (size_t(tc + row) * a.n_heads + h) * P + 8 * c) = v;
+      }
+    }
+  };
+
+  const int t_beg = a.seg_off[seg], t_end = a.seg_off[seg + 1];
+  fetch(t_beg, t_end, 0);
+  int s = 0, prev_t0 = -1, prev_n = 0;
+  for (int t0 = t_beg;;) {
+    const int n = min(L, t_end - t0);
+    const int nt0 = t0 + L;
+    const bool more = nt0 < t_end;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of the chunk has landed
+    __syncthreads();                                   // ... and every other wave's
+    if (more) fetch(nt0, t_end, s ^ 1);
+    if (prev_t0 >= 0) store_y(prev_t0, prev_n, s ^ 1);
+    const char* Bs = sm.bt[s];
+    const char* Cs = sm.ct[s];
+
+    // -- C B^T (exact), C S0 (S0 as hi + lo)
+    f32x4 qkt = z4(), cs = z4();
+#pragma unroll
+    for (int m = 0; m < NT / 2; ++m) {
+      const uint4 ac = tile_a8(Cs, ao[m], ao2[m]);
+      const uint4 ab = tile_a8(Bs, ao[m], ao2[m]);
+      qkt = mma32(ab, ac, qkt);
+      uint4 sh, sl;
+      split8m(St[2 * m], St[2 * m + 1], negI, sh, sl);
+      cs = mma32(ac, sl, mma32(ac, sh, cs));
+    }
+
+    // -- gates: G = prefix of g = dt A over the chunk (DPP scan over each row
+    //    of 16 lanes); padding rows have dt = 0
+    Gates gt;
+    {
+      const float dti = i16 < n ? sm.dt[s][i16] : 0.f;
+      float G = dti * Ah;
+      G += dpp<0x111>(G);
+      G += dpp<0x112>(G);
+      G += dpp<0x114>(G);
+      G += dpp<0x118>(G);
+      const int base = 16 * h4;
+      const float glast = __shfl(G, base + 15, 64) * kLog2e, gc = G * kLog2e;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * h4 + r;
+        const float gr = __shfl(G, base + row, 64) * kLog2e;
+        gt.gam[r] = ex2(gr);
+        gt.del[r] = ex2(glast - gr);
+        gt.bet[r] = __shfl(dti, base + row, 64);
+        gt.Gmt[r] = i16 >= row ? ex2(gc - gr) : 0.f;
+      }
+      gt.gam_last = ex2(glast);
+    }
+    const f32x4 xv = bf4(tile_tr(sm.xt[s], xo));
+    f32x4 Pt, U;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      Pt[r] = qkt[r] * gt.Gmt[r];
+      U[r] = gt.bet[r] * xv[r];
+    }
+    const f32x4 Y = mm(Pt, U, gt.gam * cs) + Dh * xv;
+    {
+      const uint2 yp = pack4(Y);
+      uint16_t* yr = &sm.ys[s][(4 * h4) * P + col];
+      yr[0] = static_cast<uint16_t>(yp.x);
+      yr[P] = static_cast<uint16_t>(yp.x >> 16);
+      yr[2 * P] = static_cast<uint16_t>(yp.y);
+      yr[3 * P] = static_cast<uint16_t>(yp.y >> 16);
+    }
+    // -- S = gamma_last S + B^T diag(delta) U
+    uint2 uh, ul;
+    split4(gt.del * U, uh, ul);
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      const uint2 ab = tile_tr(Bs, bo[rt >> 1] + 32 * (rt & 1));
+      St[rt] = mma16b(ab, ul, mma16b(ab, uh, gt.gam_last * St[rt]));
+    }
+    prev_t0 = t0;
+    prev_n = n;
+    if (!more) break;
+    t0 = nt0;
+    s ^= 1;
+  }
+  __syncthreads();  // the last chunk's staged rows
+  store_y(prev_t0, prev_n, s);
+
+  float* dst = a.states ? a.states + (size_t(seg) * a.n_heads + h) * hs
+                        : (a.slot[seg] >= 0 ? a.slots + (size_t(a.slot[seg]) * a.n_heads + h) * hs : nullptr);
+  if (dst) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[size_t(16 * rt + 4 * h4 + r) * P + col] = St[rt][r];
+  }
+}
+
 template <int N, int P, bool F32IN>
 hipError_t launch_ssd(const SsdArgs& a, hipStream_t stream) {
   if (a.n_items <= 0) return hipSuccess;
-  ssd_level_kernel<N, P, F32IN><<<dim3(unsigned(a.n_items * a.n_heads)), dim3(4 * P), 0, stream>>>(a);
+  const dim3 grid(unsigned(a.n_items * a.n_heads)), block(4 * P);
+  if constexpr (N == 128 && !F32IN)
+    ssd_bf16_n128_kernel<P><<<grid, block, 0, stream>>>(a);
+  else
+    ssd_level_kernel<N, P, F32IN><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }
 
