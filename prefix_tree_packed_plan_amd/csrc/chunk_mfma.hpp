@@ -120,6 +120,7 @@ __device__ __forceinline__ int tile_off(int row, int col) {
 __device__ __forceinline__ int tile_dma_chunk(int ln) { return (ln & 15) ^ (4 * (ln >> 4)); }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const u32x2 lds_cu2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;

@@ -293,15 +293,18 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
                                                0, 0);
     }
   };
-  // Whole rows of the staged outputs of the chunk at tc (n rows).
+  // Whole rows of the staged outputs of the chunk at tc (n rows), through a
+  // buffer descriptor whose range ends after row n - 1, so padding rows are
+  // dropped.  (Plain stores through the generic output pointer made the
+  // compiler wait for every outstanding load, the next chunk's DMA included,
+  // before the following LDS reads.)
   auto store_y = [&](int tc, int n, int buf) {
     constexpr int CPR = 2 * P / 16;  // 16-byte chunks per row
+    const auto ry = rsrc(yg + (size_t(tc) * a.n_heads + h) * P, (n - 1) * rs_x + 2 * P);
     for (int e = tid; e < L * CPR; e += 4 * P) {
       const int row = e / CPR, c = e % CPR;
-      if (row < n) {
-        const uint4 v = *reinterpret_cast<const uint4*>(&sm.ys[buf][row * P + 8 * c]);
-        *reinterpret_cast<uint4*>(yg + (size_t(tc + row) * a.n_heads + h) * P + 8 * c) = v;
-      }
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.ys[buf][row * P + 8 * c]);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ry, row * rs_x + 16 * c, 0, 0);
     }
   };
 
@@ -314,10 +317,17 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     const bool more = nt0 < t_end;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA of the chunk has landed
     __syncthreads();                                   // ... and every other wave's
-    if (more) fetch(nt0, t_end, s ^ 1);
-    if (prev_t0 >= 0) store_y(prev_t0, prev_n, s ^ 1);
     const char* Bs = sm.bt[s];
     const char* Cs = sm.ct[s];
+    // The chunk's transposing reads (x, and B^T for the state update) come
+    // before the next chunk's DMA is issued: after it, the compiler makes them
+    // wait for that DMA to land, which would serialise the prefetch.
+    const uint2 xr = tile_tr(sm.xt[s], xo);
+    uint2 bT[NT];
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) bT[rt] = tile_tr(Bs, bo[rt >> 1] + 32 * (rt & 1));
+    if (more) fetch(nt0, t_end, s ^ 1);
+    if (prev_t0 >= 0) store_y(prev_t0, prev_n, s ^ 1);
 
     // -- C B^T (exact), C S0 (S0 as hi + lo)
     f32x4 qkt = z4(), cs = z4();
@@ -354,7 +364,7 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
       }
       gt.gam_last = ex2(glast);
     }
-    const f32x4 xv = bf4(tile_tr(sm.xt[s], xo));
+    const f32x4 xv = bf4(xr);
     f32x4 Pt, U;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -375,8 +385,7 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     split4(gt.del * U, uh, ul);
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-      const uint2 ab = tile_tr(Bs, bo[rt >> 1] + 32 * (rt & 1));
-      St[rt] = mma16b(ab, ul, mma16b(ab, uh, gt.gam_last * St[rt]));
+      St[rt] = mma16b(bT[rt], ul, mma16b(bT[rt], uh, gt.gam_last * St[rt]));
     }
     prev_t0 = t0;
     prev_n = n;
