@@ -37,8 +37,10 @@
 // Precision: q, k, v and the Gram matrices are exact in bf16 x bf16 -> fp32.
 // Products that feed the state (K S0, the triangular solve, K^T U) carry each
 // fp32 operand as hi + lo bf16 (x = hi + lo to 2^-17 |x|; the lo x lo term is
-// dropped), which keeps the segment states within ~1e-5 of fp32; the output
-// path (Q S0, P U) uses hi parts only.  fp32 inputs are split the same way.
+// dropped), which keeps the segment states within ~1e-5 of fp32; for bf16
+// inputs the output path (Q S0, P U) uses hi parts only.  fp32 inputs are
+// split the same way, and their output path carries Q S0 and P U as hi + lo
+// too, so fp32 outputs are accurate to fp32 level as well.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -154,7 +156,8 @@ struct Smem {
   // inverses' input).
   alignas(16) uint32_t a[G][CH * AS];
   alignas(16) uint32_t tb[G][4][16 * 20];  // (I + A_bb)^-1, packed hi|lo
-  alignas(16) short p[G][CH * TS];         // (Q K^T) o Gamma, lower incl. diagonal, bf16
+  alignas(16) short p[G][CH * TS];         // (Q K^T) o Gamma, lower incl. diagonal, bf16 (hi part for fp32 inputs)
+  alignas(16) short pl[F32IN ? G : 1][F32IN ? CH * TS : 8];  // its lo part (fp32 inputs)
   alignas(16) float g2[G][CH];             // G * log2(e)
   alignas(16) float gam[G][CH];            // exp(G)
   alignas(16) float bet[G][CH];
@@ -404,7 +407,9 @@ __global__ __launch_bounds__(64 * G * (DV / 32)) void gdn_level_kernel(ScanArgs 
         for (int r = 0; r < 4; ++r) {
           const int i = i0 + r;
           const float val = j <= i ? acc[r] * ex2(g2i[r] - g2j) : 0.f;
-          sm.p[vh][i * SM::TS + j] = static_cast<short>(pk2(val, 0.f) & 0xffffu);
+          const uint32_t hw = pk2(val, 0.f);
+          sm.p[vh][i * SM::TS + j] = static_cast<short>(hw & 0xffffu);
+          if constexpr (F32IN) sm.pl[vh][i * SM::TS + j] = static_cast<short>(pk2(val - lo_f(hw), 0.f) & 0xffffu);
         }
       }
       if (it == BPW - 1) {
@@ -543,6 +548,14 @@ __global__ __launch_bounds__(64 * G * (DV / 32)) void gdn_level_kernel(ScanArgs 
         const uint2 ap = *reinterpret_cast<const uint2*>(&sm.p[vh][(16 * mr + i16) * SM::TS + 16 * c + 4 * h4]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) O[mr][nt] = mma16(ap, uh[nt], O[mr][nt]);
+        if constexpr (F32IN) {  // fp32 outputs: P and U as hi + lo as well
+          const uint2 apl = *reinterpret_cast<const uint2*>(&sm.pl[vh][(16 * mr + i16) * SM::TS + 16 * c + 4 * h4]);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            O[mr][nt] = mma16(ap, ul[nt], O[mr][nt]);
+            O[mr][nt] = mma16(apl, uh[nt], O[mr][nt]);
+          }
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
