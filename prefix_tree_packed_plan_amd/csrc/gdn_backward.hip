@@ -52,6 +52,8 @@
 // operand of a product with X on the left.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "../../include/tree_gdn.h"
 #include "chunk_mfma.hpp"
 #include "launch.hpp"
@@ -170,35 +172,59 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_states_kernel(ScanBwdArgs a)
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) St[rt] = z4();
     }
-    // Inputs and T^T of chunk c in registers, fetched one chunk ahead.
-    f32x4 kv, vt, Ttn;
-    float gv = 0.f, bv = 0.f;
+    // Inputs and T^T of chunk c in registers, fetched one chunk ahead as raw
+    // words from rows clamped into the chunk, unconditionally; the conversion
+    // and the zeroing of rows past the segment end wait for the use.  (Loads
+    // converted where they are issued made the compiler wait for each at once,
+    // and with it for the chunk-state stores issued just before.)
+    using KRaw = typename std::conditional<F32IN, f32x4, uint2>::type;
+    using VRaw = typename std::conditional<F32IN, float, uint16_t>::type;
+    KRaw kraw;
+    VRaw vraw[4];
+    f32x4 Ttn;
+    float graw = 0.f, braw = 0.f;
+    int nf = 0;  // rows of the fetched chunk
     auto fetch = [&](int c) {
       const int t0 = t_beg + c * L;
-      const int n = min(L, t_end - t0);
-      const bool in = st_row < n;
-      kv = in ? load4<F32IN>(a.k, (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col) : z4();
+      nf = min(L, t_end - t0);
+      kraw = *reinterpret_cast<const KRaw*>(static_cast<const VRaw*>(a.k) +
+                                            (size_t(t0 + min(st_row, nf - 1)) * a.h_qk + hq) * D + st_col);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * h4 + r;
-        vt[r] = row < n ? load1<F32IN>(a.v, (size_t(t0 + row) * a.h_v + h) * D + col) : 0.f;
+        vraw[r] = static_cast<const VRaw*>(a.v)[(size_t(t0 + min(row, nf - 1)) * a.h_v + h) * D + col];
         Ttn[r] = tws[c * tstride + i16 * L + row];
       }
       if (tid < L) {
-        const bool tin = tid < n;
-        gv = tin ? a.g[size_t(t0 + tid) * a.h_v + h] : 0.f;
-        bv = tin ? a.beta[size_t(t0 + tid) * a.h_v + h] : 0.f;
+        const size_t gi = size_t(t0 + min(tid, nf - 1)) * a.h_v + h;
+        graw = a.g[gi];
+        braw = a.beta[gi];
       }
     };
     fetch(0);
     for (int c = 0; c < nc; ++c) {
       store_ws(hws + c * cstride, St);
+      f32x4 kv, vc;
+      if constexpr (F32IN) {
+        kv = kraw;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vc[r] = vraw[r];
+      } else {
+        kv = f32x4{__uint_as_float(kraw.x << 16), __uint_as_float(kraw.x & 0xffff0000u),
+                   __uint_as_float(kraw.y << 16), __uint_as_float(kraw.y & 0xffff0000u)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vc[r] = __uint_as_float(uint32_t(vraw[r]) << 16);
+      }
+      if (st_row >= nf) kv = z4();
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * h4 + r >= nf) vc[r] = 0.f;
       *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
       if (tid < L) {
-        sm.g[tid] = gv;
-        sm.b[tid] = bv;
+        sm.g[tid] = tid < nf ? graw : 0.f;
+        sm.b[tid] = tid < nf ? braw : 0.f;
       }
-      const f32x4 vc = vt, Tt = Ttn;
+      const f32x4 Tt = Ttn;
       __syncthreads();
       if (c + 1 < nc) fetch(c + 1);
       const Gates gt = make_gates(sm.g, sm.b, h4, i16);
@@ -307,8 +333,17 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
   // Chunk c's T / T^T / KK / QK tiles and inputs, fetched one chunk ahead
   // (the start state itself is loaded at the chunk top: holding it a chunk
   // ahead costs more registers than the kernel has).
-  f32x4 Tn, Ttn, KKn, QKn, qv, kv, ov, vn;
-  float gv = 0.f, bv = 0.f;
+  // The inputs come as raw words from rows clamped into the chunk, loaded
+  // unconditionally; their conversion and the zeroing of rows past the
+  // segment end wait for the chunk top.  (Loads converted where they are
+  // issued made the compiler wait for each at once, and with it for the
+  // gradient stores issued just before.)
+  using KRaw = typename std::conditional<F32IN, f32x4, uint2>::type;
+  using VRaw = typename std::conditional<F32IN, float, uint16_t>::type;
+  f32x4 Tn, Ttn, KKn, QKn;
+  KRaw qraw, kraw, oraw;
+  VRaw vraw[4];
+  float graw = 0.f, braw = 0.f;
   auto fetch = [&](int c) {
     const int t0 = t_beg + c * L;
     const int n = min(L, t_end - t0);
@@ -321,22 +356,27 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
       KKn[r] = tp[L * L + e];
       QKn[r] = tp[2 * L * L + e];
     }
-    const bool in = st_row < n;
-    const size_t qi = (size_t(t0 + st_row) * a.h_qk + hq) * D + st_col;
-    const size_t oi = (size_t(t0 + st_row) * a.h_v + h) * D + st_col;
-    qv = in ? load4<F32IN>(a.q, qi) : z4();
-    kv = in ? load4<F32IN>(a.k, qi) : z4();
-    ov = in ? load4<F32IN>(a.dout, oi) : z4();
+    const int srow = t0 + min(st_row, n - 1);
+    const size_t qi = (size_t(srow) * a.h_qk + hq) * D + st_col;
+    const size_t oi = (size_t(srow) * a.h_v + h) * D + st_col;
+    qraw = *reinterpret_cast<const KRaw*>(static_cast<const VRaw*>(a.q) + qi);
+    kraw = *reinterpret_cast<const KRaw*>(static_cast<const VRaw*>(a.k) + qi);
+    oraw = *reinterpret_cast<const KRaw*>(static_cast<const VRaw*>(a.dout) + oi);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * h4 + r;
-      vn[r] = row < n ? load1<F32IN>(a.v, (size_t(t0 + row) * a.h_v + h) * D + col) : 0.f;
-    }
+    for (int r = 0; r < 4; ++r)
+      vraw[r] = static_cast<const VRaw*>(a.v)[(size_t(t0 + min(4 * h4 + r, n - 1)) * a.h_v + h) * D + col];
     if (tid < L) {
-      const bool tin = tid < n;
-      gv = tin ? a.g[size_t(t0 + tid) * a.h_v + h] : 0.f;
-      bv = tin ? a.beta[size_t(t0 + tid) * a.h_v + h] : 0.f;
+      const size_t gi = size_t(t0 + min(tid, n - 1)) * a.h_v + h;
+      graw = a.g[gi];
+      braw = a.beta[gi];
     }
+  };
+  auto unpack = [](const KRaw x) -> f32x4 {
+    if constexpr (F32IN)
+      return x;
+    else
+      return f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u), __uint_as_float(x.y << 16),
+                   __uint_as_float(x.y & 0xffff0000u)};
   };
   fetch(nc - 1);
 
@@ -346,13 +386,27 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     const float* s0p = hws + c * cstride;
     f32x4 S0[NT];
     load_ws(s0p, S0);
-    const f32x4 T = Tn, Tt = Ttn, kk = KKn, qk = QKn, vt = vn;
-    *reinterpret_cast<f32x4*>(&sm.q[st_row * S + st_col]) = qv;
-    *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
-    *reinterpret_cast<f32x4*>(&sm.o[st_row * S + st_col]) = F32IN ? ov * a.scale : ov;
+    const f32x4 T = Tn, Tt = Ttn, kk = KKn, qk = QKn;
+    f32x4 vt;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x;
+      if constexpr (F32IN)
+        x = vraw[r];
+      else
+        x = __uint_as_float(uint32_t(vraw[r]) << 16);
+      vt[r] = 4 * h4 + r < n ? x : 0.f;
+    }
+    {
+      const bool in = st_row < n;
+      const f32x4 qv = in ? unpack(qraw) : z4(), kv = in ? unpack(kraw) : z4(), ov = in ? unpack(oraw) : z4();
+      *reinterpret_cast<f32x4*>(&sm.q[st_row * S + st_col]) = qv;
+      *reinterpret_cast<f32x4*>(&sm.k[st_row * S + st_col]) = kv;
+      *reinterpret_cast<f32x4*>(&sm.o[st_row * S + st_col]) = F32IN ? ov * a.scale : ov;
+    }
     if (tid < L) {
-      sm.g[tid] = gv;
-      sm.b[tid] = bv;
+      sm.g[tid] = tid < n ? graw : 0.f;
+      sm.b[tid] = tid < n ? braw : 0.f;
     }
     {
       float* const dsw = &sm.ds[4 * h4 * S + col];
