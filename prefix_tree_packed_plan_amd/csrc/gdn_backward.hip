@@ -330,9 +330,10 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     for (int rt = 0; rt < NT; ++rt) dS[rt] += x[rt];
   }
 
-  // Chunk c's T / T^T / KK / QK tiles and inputs, fetched one chunk ahead
-  // (the start state itself is loaded at the chunk top: holding it a chunk
-  // ahead costs more registers than the kernel has).
+  // Chunk c's inputs, fetched one chunk ahead; its start state and its T /
+  // T^T / KK / QK tiles are loaded at the chunk top (held a chunk ahead, they
+  // push the kernel past its registers, and every spill reload waits for all
+  // outstanding loads and stores).
   // The inputs come as raw words from rows clamped into the chunk, loaded
   // unconditionally; their conversion and the zeroing of rows past the
   // segment end wait for the chunk top.  (Loads converted where they are
@@ -340,22 +341,12 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
   // gradient stores issued just before.)
   using KRaw = typename std::conditional<F32IN, f32x4, uint2>::type;
   using VRaw = typename std::conditional<F32IN, float, uint16_t>::type;
-  f32x4 Tn, Ttn, KKn, QKn;
   KRaw qraw, kraw, oraw;
   VRaw vraw[4];
   float graw = 0.f, braw = 0.f;
   auto fetch = [&](int c) {
     const int t0 = t_beg + c * L;
     const int n = min(L, t_end - t0);
-    const float* tp = tws + c * tstride;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = (4 * h4 + r) * L + i16;
-      Tn[r] = tp[e];
-      Ttn[r] = tp[i16 * L + 4 * h4 + r];
-      KKn[r] = tp[L * L + e];
-      QKn[r] = tp[2 * L * L + e];
-    }
     const int srow = t0 + min(st_row, n - 1);
     const size_t qi = (size_t(srow) * a.h_qk + hq) * D + st_col;
     const size_t oi = (size_t(srow) * a.h_v + h) * D + st_col;
@@ -386,7 +377,18 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     const float* s0p = hws + c * cstride;
     f32x4 S0[NT];
     load_ws(s0p, S0);
-    const f32x4 T = Tn, Tt = Ttn, kk = KKn, qk = QKn;
+    f32x4 T, Tt, kk, qk;
+    {
+      const float* tp = tws + c * tstride;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = (4 * h4 + r) * L + i16;
+        T[r] = tp[e];
+        Tt[r] = tp[i16 * L + 4 * h4 + r];
+        kk[r] = tp[L * L + e];
+        qk[r] = tp[2 * L * L + e];
+      }
+    }
     f32x4 vt;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
