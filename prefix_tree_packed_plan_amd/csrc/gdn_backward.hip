@@ -344,19 +344,26 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
   VRaw vraw[4];
   float graw = 0.f, braw = 0.f;
   auto fetch = [&](int c) {
+    // Lane-dependent offsets from an opaque copy of the thread id, recomputed
+    // here rather than held (spilled) across the chunk: a spill reload waits
+    // for every outstanding load and store.
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    const int ln = tl & 63, lh4 = ln >> 4, lcol = 16 * (tl >> 6) + (ln & 15);
+    const int lrow = tl / (D / 4), lcol4 = 4 * (tl % (D / 4));
     const int t0 = t_beg + c * L;
     const int n = min(L, t_end - t0);
-    const int srow = t0 + min(st_row, n - 1);
-    const size_t qi = (size_t(srow) * a.h_qk + hq) * D + st_col;
-    const size_t oi = (size_t(srow) * a.h_v + h) * D + st_col;
+    const int srow = t0 + min(lrow, n - 1);
+    const size_t qi = (size_t(srow) * a.h_qk + hq) * D + lcol4;
+    const size_t oi = (size_t(srow) * a.h_v + h) * D + lcol4;
     qraw = *reinterpret_cast<const KRaw*>(static_cast<const VRaw*>(a.q) + qi);
     kraw = *reinterpret_cast<const KRaw*>(static_cast<const VRaw*>(a.k) + qi);
     oraw = *reinterpret_cast<const KRaw*>(static_cast<const VRaw*>(a.dout) + oi);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      vraw[r] = static_cast<const VRaw*>(a.v)[(size_t(t0 + min(4 * h4 + r, n - 1)) * a.h_v + h) * D + col];
-    if (tid < L) {
-      const size_t gi = size_t(t0 + min(tid, n - 1)) * a.h_v + h;
+      vraw[r] = static_cast<const VRaw*>(a.v)[(size_t(t0 + min(4 * lh4 + r, n - 1)) * a.h_v + h) * D + lcol];
+    if (tl < L) {
+      const size_t gi = size_t(t0 + min(tl, n - 1)) * a.h_v + h;
       graw = a.g[gi];
       braw = a.beta[gi];
     }
@@ -474,13 +481,16 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     }
     glp = row_sum16(glp);
     if (i16 == 0) {
+      int ln = lane;  // opaque: see fetch
+      asm volatile("" : "+v"(ln));
+      const int lh4 = ln >> 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sm.rows[w][0][4 * h4 + r] = pg[r];
-        sm.rows[w][1][4 * h4 + r] = pd[r];
-        sm.rows[w][2][4 * h4 + r] = pb[r];
+        sm.rows[w][0][4 * lh4 + r] = pg[r];
+        sm.rows[w][1][4 * lh4 + r] = pd[r];
+        sm.rows[w][2][4 * lh4 + r] = pb[r];
       }
-      sm.gl[w][h4] = glp;
+      sm.gl[w][lh4] = glp;
     }
     __syncthreads();  // U, dR staged
 
