@@ -44,7 +44,10 @@
 // state gradient dS, which stays in MFMA accumulator registers across the
 // segment.
 //
-// MFMA: v_mfma_f32_16x16x4_f32 (fp32 inputs, fp32 accumulate) throughout.
+// MFMA: for bf16 inputs the dense [16, d] x [d, d] products run on
+// v_mfma_f32_16x16x32_bf16 with each fp32 operand carried as hi + lo bf16
+// (q, k and dO are exact in bf16); the [16, 16] products, the inverse and
+// every product for fp32 inputs run on v_mfma_f32_16x16x4_f32.
 // Lane l = 16 h + i (h = l / 16) holds accumulator rows 4h + r, column i.
 // A 16-deep contraction is four MFMAs; in step s lane l supplies index
 // 4h + s of the contraction, so an accumulator tile is the B operand of a
