@@ -371,7 +371,13 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
       Pt[r] = qkt[r] * gt.Gmt[r];
       U[r] = gt.bet[r] * xv[r];
     }
-    const f32x4 Y = mm(Pt, U, gt.gam * cs) + Dh * xv;
+    f32x4 Y;
+    {  // P U on split-bf16 MFMA (hi x hi + hi x lo + lo x hi)
+      uint2 ph, pl, uh2, ul2;
+      split4m(Pt, negI, ph, pl);
+      split4(U, uh2, ul2);
+      Y = mma16b(pl, uh2, mma16b(ph, ul2, mma16b(ph, uh2, gt.gam * cs))) + Dh * xv;
+    }
     {
       const uint2 yp = pack4(Y);
       uint16_t* yr = &sm.ys[s][(4 * h4) * P + col];
