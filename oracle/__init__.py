@@ -16,6 +16,11 @@ root-to-leaf path produces.  So the oracle simply runs each path on its own:
 * gdn.py   -- token-by-token gated delta rule over the path.
 * trie.py  -- parents -> children, leaves, paths, POR.
 * brute.py -- independent fp64 brute forces used to pin the above.
+* grad.py  -- gradients of the tree conv and tree gated delta rule: autograd
+              of the token-by-token tree forward (fp64), siblings' gradients
+              summed into their parent.
+* ssd.py   -- token-by-token Mamba2 (SSD) recurrence over every path, the
+              forked state of the tree Mamba2 forward.
 
 Arithmetic is fp64 by default.  Parity status of every function is pinned by
 tests (see tests/test_oracle_*.py); nothing here is "parity unpinned".
