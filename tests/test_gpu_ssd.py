@@ -32,7 +32,7 @@ def host(t):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(1, 2, 128, 64), (2, 4, 128, 32), (2, 4, 64, 32)])
+@pytest.mark.parametrize("shape", [(1, 2, 128, 64), (2, 4, 128, 64), (2, 4, 128, 32), (2, 4, 64, 32)])
 def test_ssd_matches_the_oracle(dtype, shape):
     """Ragged forest (1..40-token segments: whole 16-token chunks and tails,
     fan-outs), given root states, D on; outputs and every final state."""
