@@ -116,14 +116,16 @@ typedef struct tree_plan_stats {
  *             forest) are allowed.
  * seg_lens[i] tokens of segment i, >= 1.  Sum must be < 2^31.
  * n_seg       number of segments, >= 1.
- * conv_width  W of the causal conv, 1..8.
+ * conv_width  W of the causal conv, 1..8; n_seg (W-1) must be < 2^31.
  * out         receives a library-owned plan; free it with tree_plan_free.
  *
  * The plan holds: segment offsets; depths and the per-level segment order
  * (longest segment first within a level); the state slot of every segment
  * with children; and the conv history table hist[s][0..W-2], the packed row
- * indices of the W-1 inputs preceding segment s on its path (-1 = zero pad):
- * the last W-1 entries of hist[parent] followed by the parent's own rows.
+ * indices of the W-1 inputs preceding segment s on its path: the last W-1
+ * entries of hist[parent] followed by the parent's own rows.  A negative
+ * entry -1 - (r (W-1) + j) names context row j (oldest first) of the r-th
+ * root in segment order (init_ctx of tree_conv; zeros when that is NULL).
  * Inputs are copied; the plan is immutable and may be shared across threads.
  */
 int tree_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,

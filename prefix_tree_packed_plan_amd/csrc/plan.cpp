@@ -40,6 +40,11 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
     *err = fmt("tree_plan: conv_width must be in 1..8 (got %ld)", conv_width);
     return TREE_ERR_INVALID_ARG;
   }
+  // Conv history rows s (W-1) + j are int32 in every table and kernel.
+  if (static_cast<int64_t>(n_seg) * (conv_width - 1) >= (int64_t(1) << 31)) {
+    *err = fmt("tree_plan: n_seg (W-1) must be < 2^31 (got %ld segments, W = %ld)", n_seg, conv_width);
+    return TREE_ERR_BAD_TREE;
+  }
   Plan p;
   p.n_seg = n_seg;
   p.width = conv_width;
@@ -189,6 +194,19 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
         }
       }
     }
+    // Both CSR tables are indexed with int32 offsets on the device.
+    size_t n_ent = 0, n_fut = 0;
+    for (int32_t i = 0; i < n_seg && H > 0; ++i)
+      for (int32_t m = 0; m < H; ++m) {
+        n_ent += ent[static_cast<size_t>(i) * H + m].size();
+        for (const int32_t c : kids[i]) n_fut += ent[static_cast<size_t>(c) * H + m].size();
+      }
+    if (n_ent >= (size_t(1) << 31) || n_fut >= (size_t(1) << 31)) {
+      *err = "tree_plan: conv backward head tables exceed 2^31 entries";
+      return TREE_ERR_BAD_TREE;
+    }
+    p.ent.reserve(n_ent);
+    p.fut.reserve(n_fut);
     p.ent_off.assign(1, 0);
     p.fut_off.assign(1, 0);
     for (int32_t i = 0; i < n_seg && H > 0; ++i) {

@@ -50,7 +50,7 @@ struct Plan {
   // Conv backward: "head" rows h = s (W-1) + j name token j < W-1 of segment
   // s.  ent[s][m] (CSR over s (W-1) + m) lists the head rows of the tokens
   // m steps after segment s's first token along any path (s's own token m
-  // if it has one, else the children's, recursively); fut[s][m] those m
+  // if it has one, else the children's, recursively); fut[s][m] those m + 1
   // steps after s's last token, i.e. the union of the children's ent[c][m].
   // roots: the roots in segment order.
   std::vector<int32_t> ent_off, ent, fut_off, fut, roots;
