@@ -302,3 +302,13 @@ def test_ssd_scan_argument_checks_need_no_device():
     assert call(ws=need - 1) == -5
     assert call(x=None) == -1
     assert b"tree_ssd_scan" in lib.tree_last_error()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library every entry point raises."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libtreegdn.so"))
+    with pytest.raises(OSError, match="is missing"):
+        _lib.load()
+    with pytest.raises(OSError, match="is missing"):
+        _lib.tree_plan(np.array([-1, 0], np.int32), np.array([3, 2], np.int32), 4)
