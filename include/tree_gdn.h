@@ -311,7 +311,7 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g,
  * three [h_v, 16, 16] fp32 matrices of every 16-token chunk, one
  * start-state gradient ([h_v, d_k, d_v] fp32) per segment, plus
  * per-value-head dq and dk
- * ([n_tokens, h_v, d_k] fp32 each) when h_v != h_qk.
+ * ([n_tokens, h_v, d_k] fp32 each) when h_v > 2 h_qk.
  */
 size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h_qk, int32_t h_v, int32_t d_k,
                                               int32_t d_v);
@@ -336,7 +336,9 @@ size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h
  * states  device, [n_seg, h_v, d_k, d_v] fp32: the final states the
  *         forward wrote (tree_gdn_scan's `states`)    (read)
  * dq, dk  device, [n_tokens, h_qk, d_k] fp32 (summed over the value heads
- *         of each query/key head, in head order)      (written)
+ *         of each query/key head, in head order; with two value heads
+ *         per q/k head both add into the zeroed output, which rounds the
+ *         same in either order)                       (written)
  * dv      device, [n_tokens, h_v, d_v] fp32           (written)
  * dg, dbeta device, [n_tokens, h_v] fp32              (written)
  * dinit_states device, [n_roots, h_v, d_k, d_v] fp32, or NULL (written)

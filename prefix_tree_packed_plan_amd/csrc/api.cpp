@@ -290,7 +290,7 @@ size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h
   const size_t dd = static_cast<size_t>(d_k) * d_v;
   size_t n = (static_cast<size_t>(p.total_chunks) + p.n_seg) * h_v * dd;
   n += static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
-  if (h_v != h_qk) n += 2 * static_cast<size_t>(p.n_tokens) * h_v * d_k;
+  if (h_v > 2 * h_qk) n += 2 * static_cast<size_t>(p.n_tokens) * h_v * d_k;  // per-value-head dq, dk
   return n * sizeof(float);
 }
 
@@ -338,10 +338,14 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.dsseg = a.hws + static_cast<size_t>(p.total_chunks) * h_v * dd;
   a.tws = a.dsseg + static_cast<size_t>(p.n_seg) * h_v * dd;
   float* per_head = a.tws + static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
-  const bool grouped = h_v != h_qk;
+  // One value head per q/k head: dq, dk written directly.  Two: both add
+  // into zeroed dq, dk.  More: per-value-head parts, summed in head order.
+  const bool pairwise = h_v == 2 * h_qk;
+  const bool grouped = h_v > 2 * h_qk;
   a.dq = grouped ? per_head : dq;
   a.dk = grouped ? per_head + static_cast<size_t>(n_tokens) * h_v * d_k : dk;
   a.dq_heads = grouped ? h_v : h_qk;
+  a.dq_accum = pairwise ? 1 : 0;
   a.seg_off = base + p.m_seg_off;
   a.parent = base + p.m_parent;
   a.root_idx = base + p.m_root;
@@ -355,6 +359,12 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.h_v = h_v;
   a.scale = scale;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pairwise) {
+    const int64_t n = n_tokens * h_qk * d_k;
+    hipError_t e = tg::launch_zero_f32(dq, n, st);
+    if (e == hipSuccess) e = tg::launch_zero_f32(dk, n, st);
+    if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);
+  }
   {
     const hipError_t e = tg::launch_scan_backward_prep(a, d_k, dtype, st);
     if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);

@@ -591,12 +591,21 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     dK = mm(dKKt, kc, dK);
     dK = mm(dKK, kc, dK);
     dK = dK + xu - gt.gam * xv;
+    // With two value heads per q/k head, each adds its part into the zeroed
+    // dq, dk: 0 + a + b rounds the same in either order, so the sum is
+    // deterministic and equal to the ordered head-group sum.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * h4 + r;
       if (row < n) {
-        a.dq[(size_t(t0 + row) * a.dq_heads + dq_head) * D + col] = dQ[r];
-        a.dk[(size_t(t0 + row) * a.dq_heads + dq_head) * D + col] = dK[r];
+        const size_t o = (size_t(t0 + row) * a.dq_heads + dq_head) * D + col;
+        if (a.dq_accum) {
+          unsafeAtomicAdd(a.dq + o, dQ[r]);
+          unsafeAtomicAdd(a.dk + o, dK[r]);
+        } else {
+          a.dq[o] = dQ[r];
+          a.dk[o] = dK[r];
+        }
       }
     }
     const f32x4 gdo = gt.gam * dOc, gdv = -(gt.gam * dV);
@@ -781,6 +790,18 @@ hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hi
     case 128: return f32 ? launch_bwd_level<128, true>(a, stream) : launch_bwd_level<128, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+__global__ void zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int threads = 256;
+  zero_f32<<<dim3(unsigned((n + threads - 1) / threads)), dim3(threads), 0, stream>>>(p, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_head_group_sum(const float* src, float* dst, int64_t n_tok, int h_qk, int group, int d,

@@ -107,7 +107,7 @@ GRAD_NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dinit")
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 32), ("bf16", 64), ("bf16", 128)])
-@pytest.mark.parametrize("heads", [(1, 1), (1, 2)])
+@pytest.mark.parametrize("heads", [(1, 1), (1, 2), (2, 4), (1, 4)])
 def test_scan_backward_matches_the_oracle(dtype, d, heads):
     """Ragged forest (segments of 1..40 tokens: whole 16-token chunks and
     tails, chains and fan-outs), given root states and final-state
