@@ -338,8 +338,9 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.dsseg = a.hws + static_cast<size_t>(p.total_chunks) * h_v * dd;
   a.tws = a.dsseg + static_cast<size_t>(p.n_seg) * h_v * dd;
   float* per_head = a.tws + static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
-  // One value head per q/k head: dq, dk written directly.  Two: both add
-  // into zeroed dq, dk.  More: per-value-head parts, summed in head order.
+  // One value head per q/k head: dq, dk written directly.  Two: the prep
+  // launch clears dq, dk and both heads add into them.  More: per-value-head
+  // parts, summed in head order.
   const bool pairwise = h_v == 2 * h_qk;
   const bool grouped = h_v > 2 * h_qk;
   a.dq = grouped ? per_head : dq;
@@ -359,12 +360,6 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.h_v = h_v;
   a.scale = scale;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (pairwise) {
-    const int64_t n = n_tokens * h_qk * d_k;
-    hipError_t e = tg::launch_zero_f32(dq, n, st);
-    if (e == hipSuccess) e = tg::launch_zero_f32(dk, n, st);
-    if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);
-  }
   {
     const hipError_t e = tg::launch_scan_backward_prep(a, d_k, dtype, st);
     if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);

@@ -732,6 +732,15 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(ScanBwdArgs a) {
     tp[L * L + e] = kk[r];
     tp[2 * L * L + e] = qk[r];
   }
+  // Two value heads per q/k head add into dq and dk in the level launches:
+  // the first of the pair clears the chunk's rows here, before them.
+  if (a.dq_accum && (h & 1) == 0) {
+    for (int e = lane; e < n * D; e += 64) {
+      const size_t o = (size_t(t0 + e / D) * a.dq_heads + hq) * D + (e % D);
+      a.dq[o] = 0.f;
+      a.dk[o] = 0.f;
+    }
+  }
 }
 
 // dst[t, j, :] = sum over the G value heads of q/k head j of src[t, j G + m, :],
@@ -790,18 +799,6 @@ hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hi
     case 128: return f32 ? launch_bwd_level<128, true>(a, stream) : launch_bwd_level<128, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
-}
-
-__global__ void zero_f32(float* __restrict__ p, int64_t n) {
-  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.f;
-}
-
-hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  const int threads = 256;
-  zero_f32<<<dim3(unsigned((n + threads - 1) / threads)), dim3(threads), 0, stream>>>(p, n);
-  return hipGetLastError();
 }
 
 hipError_t launch_head_group_sum(const float* src, float* dst, int64_t n_tok, int h_qk, int group, int d,

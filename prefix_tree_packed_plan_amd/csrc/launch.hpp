@@ -126,7 +126,7 @@ struct ScanBwdArgs {
   int32_t h_qk;
   int32_t h_v;
   int32_t dq_heads;      // h_qk (dq, dk written per q/k head) or h_v (per value head)
-  int32_t dq_accum;      // 1: two value heads per q/k head add into zeroed dq, dk (dq_heads = h_qk)
+  int32_t dq_accum;      // 1: two value heads per q/k head add into dq, dk (dq_heads = h_qk), cleared by prep
   float scale;
 };
 
@@ -138,8 +138,6 @@ hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hi
 // dst[t, j] = sum_m src[t, j group + m] over [n_tok, h_qk * group, d] fp32.
 hipError_t launch_head_group_sum(const float* src, float* dst, int64_t n_tok, int h_qk, int group, int d,
                                  hipStream_t stream);
-// p[0 .. n) = 0, by a kernel (no memset node if the stream is captured).
-hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 bool scan_backward_supported(int d_k, int d_v, int dtype);
 
 struct SsdArgs {
