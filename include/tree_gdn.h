@@ -11,8 +11,8 @@
  *   - tree_conv: a short causal depthwise conv1d in which every segment reads
  *     the last W-1 inputs of its own root-to-segment path (same paper,
  *     section 3.2 "Causal convolution", Eq. 11; tree-recurrence 0.1.0 project
- *     page, "How a tree runs": the conv puts each segment's path history in
- *     front of it in one call).
+ *     page, "How a tree runs": a single conv launch covers every segment,
+ *     each one given the inputs that precede it on its path).
  *   - tree_gdn_scan: a chunked gated delta rule in which every segment starts
  *     from the final state of its parent segment and a root from zero (same
  *     paper, section 3.2 "SSM Layers (GDN)", Eq. 10; appendix A.2), so
@@ -29,7 +29,12 @@
  *     exception crosses the ABI.  tree_last_error() gives a message for the
  *     last failure on the calling thread.
  *   - Arguments are validated before any device work is enqueued; on failure
- *     nothing is written.
+ *     nothing is written.  That includes the device plan `dplan`: an entry
+ *     point accepts only a buffer that tree_plan_upload filled from the same
+ *     plan, with dplan_bytes >= tree_plan_device_bytes(plan) and no larger
+ *     than the size it was uploaded with; any other pointer is rejected
+ *     (INVALID_ARG, or WORKSPACE when dplan_bytes is too small).  The record
+ *     lives as long as the plan: free a dplan buffer only after the plan.
  *   - "device" pointers are HIP device memory owned by the caller.  The
  *     library never allocates or frees device memory.
  *   - `stream` is a hipStream_t (NULL = the default stream).  All device
@@ -160,8 +165,9 @@ int tree_plan_paths(const tree_plan_t* plan, int32_t* path_off, int32_t* path_se
 
 /*
  * tree_plan_choose_schedule -- the fork/rescan policy (tree-recurrence 0.1.0
- * project page, "How a tree runs": fork when the prefix tokens it saves
- * outweigh one more kernel call per level).  With saved = path_tokens -
+ * project page, "How a tree runs": forking pays off when the shared-prefix
+ * tokens it avoids rescanning are worth more than the extra launch each trie
+ * level costs).  With saved = path_tokens -
  * n_tokens (tokens a rescan would scan twice or more) and n_levels - 1 extra
  * launches for the fork, *sched = TREE_SCHED_LEVEL when
  *     saved >= fork_min_saved_tokens * (n_levels - 1)
@@ -180,9 +186,12 @@ size_t tree_plan_device_bytes(const tree_plan_t* plan);
  * tree_plan_upload -- copy the plan into caller-owned device memory `dplan`
  * (dplan_bytes >= tree_plan_device_bytes) with an asynchronous host-to-device
  * copy on `stream`.  Do it once per plan; every tree_conv / tree_gdn_scan that
- * names this plan then takes the same `dplan` (e.g. every layer of a forward).
+ * names this plan then takes the same `dplan` and `dplan_bytes` (e.g. every
+ * layer of a forward).  The plan records (dplan, dplan_bytes), under a lock,
+ * so that the entry points can reject any other buffer before launching.
  * The source is the plan's own pageable host buffer, so the plan must stay
  * alive until the copy has run (synchronise `stream` before freeing it).
+ * Errors: INVALID_ARG, WORKSPACE (dplan_bytes too small), HIP.
  */
 int tree_plan_upload(const tree_plan_t* plan, void* dplan, size_t dplan_bytes, void* stream);
 
@@ -211,13 +220,15 @@ int tree_plan_upload(const tree_plan_t* plan, void* dplan, size_t dplan_bytes, v
  *          from).  Ignored when W = 1.                (written)
  * dtype TREE_DTYPE_F32 or TREE_DTYPE_BF16; arithmetic in fp32.
  * act   TREE_ACT_NONE or TREE_ACT_SILU (y = z * sigmoid(z)).
- * dplan device copy of `plan` made by tree_plan_upload.
- * Errors: INVALID_ARG, SIZE (n_tokens != plan N), UNSUPPORTED (W > 4),
- * HIP.
+ * dplan, dplan_bytes  device copy of `plan` made by tree_plan_upload, and
+ *       the size it was uploaded with (see Conventions).
+ * Errors: INVALID_ARG (also: dplan not an upload of this plan), SIZE
+ * (n_tokens != plan N), UNSUPPORTED (W > 4), WORKSPACE (dplan_bytes too
+ * small), HIP.
  */
 int tree_conv(const void* x, const void* w, const void* bias, void* y, const void* init_ctx,
               void* ctx_out, int64_t n_tokens, int32_t channels, int32_t dtype, int32_t act,
-              const tree_plan_t* plan, const void* dplan, void* stream);
+              const tree_plan_t* plan, const void* dplan, size_t dplan_bytes, void* stream);
 
 /*
  * tree_conv_backward_workspace_bytes -- device workspace tree_conv_backward
@@ -251,13 +262,14 @@ size_t tree_conv_backward_workspace_bytes(const tree_plan_t* plan, int32_t chann
  * dw        device, [channels, W] fp32                (written)
  * dbias     device, [channels] fp32, or NULL          (written)
  * dinit_ctx device, [n_roots, W-1, channels] fp32, or NULL (written; W > 1)
+ * dplan, dplan_bytes  as for tree_conv.
  * ws        device workspace of ws_bytes >= tree_conv_backward_workspace_bytes.
  * Errors: INVALID_ARG, SIZE, UNSUPPORTED (W > 4), WORKSPACE, HIP.
  */
 int tree_conv_backward(const void* x, const void* w, const void* bias, const void* dy, const void* init_ctx,
                        void* dx, float* dw, float* dbias, float* dinit_ctx, int64_t n_tokens, int32_t channels,
-                       int32_t dtype, int32_t act, const tree_plan_t* plan, const void* dplan, void* ws,
-                       size_t ws_bytes, void* stream);
+                       int32_t dtype, int32_t act, const tree_plan_t* plan, const void* dplan, size_t dplan_bytes,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tree_scan_workspace_bytes -- device workspace tree_gdn_scan needs under
@@ -267,6 +279,17 @@ int tree_conv_backward(const void* x, const void* w, const void* bias, const voi
  */
 size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d_k, int32_t d_v,
                                  int32_t with_states);
+
+/*
+ * tree_workspace_bytes -- device workspace tree_gdn_scan needs under schedule
+ * `sched` when the caller does not ask for `states` (the largest case): the
+ * parent state slots under TREE_SCHED_LEVEL, nothing under TREE_SCHED_RESCAN;
+ * TREE_SCHED_AUTO is resolved with tree_plan_choose_schedule and
+ * TREE_FORK_MIN_SAVED_TOKENS.  The device plan is not part of it: it is the
+ * separate `dplan` buffer, uploaded once per forward and shared by every
+ * call that names the plan.  0 for a NULL plan.
+ */
+size_t tree_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d_k, int32_t d_v, int32_t sched);
 
 /*
  * tree_gdn_scan -- chunked gated delta rule over the trie ("Tree Training"
@@ -292,6 +315,7 @@ size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d
  *        two bf16 parts on every product).
  * sched  TREE_SCHED_LEVEL, TREE_SCHED_RESCAN or TREE_SCHED_AUTO (see
  *        tree_plan_choose_schedule).
+ * dplan, dplan_bytes  as for tree_conv.
  * ws     device workspace of ws_bytes >= tree_scan_workspace_bytes (may be
  *        NULL under TREE_SCHED_RESCAN).
  * Compiled head sizes: d_k = d_v in {32, 128} for bf16, 32 for fp32.
@@ -302,8 +326,8 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g,
                   const float* beta, void* o, const float* init_states, float* states,
                   int64_t n_tokens, int32_t h_qk,
                   int32_t h_v, int32_t d_k, int32_t d_v, float scale, int32_t dtype,
-                  int32_t sched, const tree_plan_t* plan, const void* dplan, void* ws,
-                  size_t ws_bytes, void* stream);
+                  int32_t sched, const tree_plan_t* plan, const void* dplan, size_t dplan_bytes,
+                  void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tree_gdn_scan_backward_workspace_bytes -- device workspace
@@ -342,6 +366,7 @@ size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h
  * dv      device, [n_tokens, h_v, d_v] fp32           (written)
  * dg, dbeta device, [n_tokens, h_v] fp32              (written)
  * dinit_states device, [n_roots, h_v, d_k, d_v] fp32, or NULL (written)
+ * dplan, dplan_bytes  as for tree_conv.
  * ws      device workspace of ws_bytes >= tree_gdn_scan_backward_workspace_bytes.
  * Compiled head sizes: d_k = d_v in {32, 64, 128}; bf16 or fp32 inputs.
  * Errors: INVALID_ARG, SIZE, UNSUPPORTED, WORKSPACE, HIP.
@@ -351,7 +376,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
                            const float* states, float* dq, float* dk, float* dv, float* dg, float* dbeta,
                            float* dinit_states, int64_t n_tokens, int32_t h_qk, int32_t h_v, int32_t d_k,
                            int32_t d_v, float scale, int32_t dtype, const tree_plan_t* plan, const void* dplan,
-                           void* ws, size_t ws_bytes, void* stream);
+                           size_t dplan_bytes, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * tree_ssd_scan -- Mamba2 (SSD) forward with the state forked over the trie
@@ -374,6 +399,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
  *                                                          (read)
  * states device, [n_seg, n_heads, d_state, head_dim] fp32, or NULL: every
  *        segment's final state (then the workspace may be empty)  (written)
+ * dplan, dplan_bytes  as for tree_conv.
  * ws     device workspace of ws_bytes >= tree_scan_workspace_bytes(plan,
  *        n_heads, d_state, head_dim, states != NULL).
  * dtype  TREE_DTYPE_BF16 (bf16 MFMA; the products with the state take it as
@@ -384,7 +410,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
 int tree_ssd_scan(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
                   void* y, const float* init_states, float* states, int64_t n_tokens, int32_t n_groups,
                   int32_t n_heads, int32_t d_state, int32_t head_dim, int32_t dtype, const tree_plan_t* plan,
-                  const void* dplan, void* ws, size_t ws_bytes, void* stream);
+                  const void* dplan, size_t dplan_bytes, void* ws, size_t ws_bytes, void* stream);
 
 /* Message for the last failed call on this thread ("" if none). */
 const char* tree_last_error(void);

@@ -61,18 +61,19 @@ SIGNATURES = {
     "tree_plan_choose_schedule": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_I32)]),
     "tree_plan_device_bytes": (_SZ, [_P]),
     "tree_plan_upload": (ctypes.c_int, [_P, _P, _SZ, _P]),
-    "tree_conv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]),
+    "tree_conv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "tree_conv_backward_workspace_bytes": (_SZ, [_P, _I32]),
-    "tree_conv_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P,
-                                          _SZ, _P]),
+    "tree_conv_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _SZ,
+                                          _P, _SZ, _P]),
     "tree_scan_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
+    "tree_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
     "tree_gdn_scan": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
-                                     _F, _I32, _I32, _P, _P, _P, _SZ, _P]),
+                                     _F, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "tree_gdn_scan_backward_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
     "tree_gdn_scan_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
-                                              _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _P, _SZ, _P]),
+                                              _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _SZ, _P, _SZ, _P]),
     "tree_ssd_scan": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32,
-                                     _P, _P, _P, _SZ, _P]),
+                                     _P, _P, _SZ, _P, _SZ, _P]),
     "tree_last_error": (ctypes.c_char_p, []),
 }
 
@@ -233,6 +234,26 @@ def _need(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _need_shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(workspace, need, dev):
+    """The caller's workspace (a device tensor of at least `need` bytes) or a
+    new one; returns (tensor or None, bytes)."""
+    import torch
+    if workspace is None:
+        if need <= 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace has {nbytes} bytes, needs {need}")
+    return workspace, nbytes
+
+
 def tree_conv(x, w, plan: TreePlan, bias=None, act: Optional[str] = None, out=None,
               init_ctx=None, return_ctx: bool = False, ctx_out=None):
     """y = tree-aware causal depthwise conv of x [N, C] with w [C, W].
@@ -243,10 +264,11 @@ def tree_conv(x, w, plan: TreePlan, bias=None, act: Optional[str] = None, out=No
     import torch
     _need(x, "x")
     _need(w, "w", x.dtype, x.device)
-    if bias is not None:
-        _need(bias, "bias", x.dtype, x.device)
     if x.dim() != 2 or w.dim() != 2 or w.shape[0] != x.shape[1] or w.shape[1] != plan.conv_width:
         raise ValueError("shapes must be x [N, C], w [C, W] with W = plan conv width")
+    if bias is not None:
+        _need(bias, "bias", x.dtype, x.device)
+        _need_shape(bias, "bias", (x.shape[1],))
     w1 = plan.conv_width - 1
     if init_ctx is not None:
         _need(init_ctx, "init_ctx", x.dtype, x.device)
@@ -260,13 +282,15 @@ def tree_conv(x, w, plan: TreePlan, bias=None, act: Optional[str] = None, out=No
             raise ValueError("ctx_out must be [n_seg, W-1, C]")
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", x.dtype, x.device)
+    _need_shape(y, "out", x.shape)
     a = {None: ACT_NONE, "none": ACT_NONE, "silu": ACT_SILU, "swish": ACT_SILU}[act]
     dplan = plan.on_device(x.device)
     stream = torch.cuda.current_stream(x.device).cuda_stream
     _check(load().tree_conv(x.data_ptr(), w.data_ptr(), bias.data_ptr() if bias is not None else None,
                             y.data_ptr(), init_ctx.data_ptr() if init_ctx is not None else None,
                             ctx_out.data_ptr() if ctx_out is not None else None,
-                            x.shape[0], x.shape[1], _dtype_code(x), a, plan.handle, dplan.data_ptr(), stream))
+                            x.shape[0], x.shape[1], _dtype_code(x), a, plan.handle, dplan.data_ptr(),
+                            dplan.numel(), stream))
     if return_ctx:
         return y, ctx_out
     return y
@@ -290,26 +314,27 @@ def tree_conv_backward(x, w, dy, plan: TreePlan, bias=None, act: Optional[str] =
         raise ValueError("w's width must be the plan's conv width")
     if bias is not None:
         _need(bias, "bias", x.dtype, dev)
+        _need_shape(bias, "bias", (c,))
     if init_ctx is not None:
         _need(init_ctx, "init_ctx", x.dtype, dev)
         if tuple(init_ctx.shape) != (plan.n_roots, w1, c):
             raise ValueError("init_ctx must be [n_roots, W-1, C]")
     dx = torch.empty_like(x) if dx is None else dx
     _need(dx, "dx", x.dtype, dev)
+    _need_shape(dx, "dx", x.shape)
     dw = torch.empty((c, w1 + 1), dtype=torch.float32, device=dev)
     db = torch.empty(c, dtype=torch.float32, device=dev) if bias is not None else None
     dctx = torch.empty((plan.n_roots, w1, c), dtype=torch.float32, device=dev) if w1 > 0 else None
     lib = load()
     need = int(lib.tree_conv_backward_workspace_bytes(plan.handle, c))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     a = {None: ACT_NONE, "silu": ACT_SILU}[act]
     dplan = plan.on_device(dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     _check(lib.tree_conv_backward(x.data_ptr(), w.data_ptr(), p(bias), dy.data_ptr(), p(init_ctx), dx.data_ptr(),
                                   dw.data_ptr(), p(db), p(dctx), n, c, _dtype_code(x), a, plan.handle,
-                                  dplan.data_ptr(), workspace.data_ptr(), workspace.numel(), stream))
+                                  dplan.data_ptr(), dplan.numel(), p(workspace), ws_bytes, stream))
     return dx, dw, db, dctx
 
 
@@ -336,10 +361,12 @@ def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_s
         raise ValueError("g and beta must be [N, H_v]")
     o = torch.empty_like(v) if out is None else out
     _need(o, "out", q.dtype, dev)
+    _need_shape(o, "out", v.shape)
     if return_states and states is None:
         states = torch.empty((plan.n_seg, h_v, d_k, d_v), dtype=torch.float32, device=dev)
     if states is not None:
         _need(states, "states", torch.float32, dev)
+        _need_shape(states, "states", (plan.n_seg, h_v, d_k, d_v))
     if init_states is not None:
         _need(init_states, "init_states", torch.float32, dev)
         if tuple(init_states.shape) != (plan.n_roots, h_v, d_k, d_v):
@@ -353,17 +380,15 @@ def tree_gdn_scan(q, k, v, g, beta, plan: TreePlan, scale: float = 1.0, return_s
     need = 0
     if sched == SCHED_LEVEL:
         need = int(lib.tree_scan_workspace_bytes(plan.handle, h_v, d_k, d_v, int(states is not None)))
-    if need > 0 and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     dplan = plan.on_device(dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     _check(lib.tree_gdn_scan(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                              o.data_ptr(), init_states.data_ptr() if init_states is not None else None,
                              states.data_ptr() if states is not None else None,
                              n, h_qk, h_v, d_k, d_v, float(scale), _dtype_code(q), sched,
-                             plan.handle, dplan.data_ptr(),
-                             workspace.data_ptr() if workspace is not None else None,
-                             workspace.numel() if workspace is not None else 0, stream))
+                             plan.handle, dplan.data_ptr(), dplan.numel(),
+                             workspace.data_ptr() if workspace is not None else None, ws_bytes, stream))
     if return_states:
         return o, states
     return o
@@ -413,8 +438,7 @@ def tree_gdn_scan_backward(q, k, v, g, beta, do, plan: TreePlan, states, scale: 
     dinit = torch.empty((plan.n_roots, h_v, d_k, d_v), dtype=f32, device=dev)
     lib = load()
     need = int(lib.tree_gdn_scan_backward_workspace_bytes(plan.handle, h_qk, h_v, d_k, d_v))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     dplan = plan.on_device(dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
@@ -422,7 +446,7 @@ def tree_gdn_scan_backward(q, k, v, g, beta, do, plan: TreePlan, states, scale: 
                                       do.data_ptr(), p(dstates), p(init_states), states.data_ptr(),
                                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), db.data_ptr(),
                                       dinit.data_ptr(), n, h_qk, h_v, d_k, d_v, float(scale), _dtype_code(q),
-                                      plan.handle, dplan.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      plan.handle, dplan.data_ptr(), dplan.numel(), p(workspace), ws_bytes,
                                       stream))
     return dq, dk, dv, dg, db, dinit
 
@@ -456,25 +480,26 @@ def tree_ssd_scan(x, dt, A, B, C, plan: TreePlan, D=None, return_states: bool = 
             raise ValueError("D must be [H]")
     y = torch.empty_like(x) if out is None else out
     _need(y, "out", x.dtype, dev)
+    _need_shape(y, "out", x.shape)
     if return_states and states is None:
         states = torch.empty((plan.n_seg, n_heads, d_state, head_dim), dtype=f32, device=dev)
     if states is not None:
         _need(states, "states", f32, dev)
+        _need_shape(states, "states", (plan.n_seg, n_heads, d_state, head_dim))
     if init_states is not None:
         _need(init_states, "init_states", f32, dev)
         if tuple(init_states.shape) != (plan.n_roots, n_heads, d_state, head_dim):
             raise ValueError("init_states must be [n_roots, H, d_state, P]")
     lib = load()
     need = int(lib.tree_scan_workspace_bytes(plan.handle, n_heads, d_state, head_dim, int(states is not None)))
-    if need > 0 and (workspace is None or workspace.numel() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     dplan = plan.on_device(dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     _check(lib.tree_ssd_scan(x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(), p(D),
                              y.data_ptr(), p(init_states), p(states), n, n_groups, n_heads, d_state, head_dim,
-                             _dtype_code(x), plan.handle, dplan.data_ptr(), p(workspace),
-                             workspace.numel() if workspace is not None else 0, stream))
+                             _dtype_code(x), plan.handle, dplan.data_ptr(), dplan.numel(), p(workspace), ws_bytes,
+                             stream))
     if return_states:
         return y, states
     return y

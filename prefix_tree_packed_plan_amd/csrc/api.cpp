@@ -4,8 +4,10 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/tree_gdn.h"
 #include "launch.hpp"
@@ -13,6 +15,13 @@
 
 struct tree_plan {
   tg::Plan p;
+  // Device buffers this plan was uploaded into (tree_plan_upload) and their
+  // sizes.  The entry points accept a device plan only from this list, so a
+  // stale, short or foreign buffer is rejected on the host before any launch.
+  // The plan is otherwise immutable; the list has its own lock so that the
+  // plan can be shared across threads.
+  mutable std::mutex mu;
+  mutable std::vector<std::pair<const void*, size_t>> uploads;
 };
 
 namespace {
@@ -34,6 +43,23 @@ int hip_fail(const char* what, hipError_t e) {
 }
 
 bool dtype_ok(int32_t d) { return d == TREE_DTYPE_F32 || d == TREE_DTYPE_BF16; }
+
+// The device plan passed to an entry point must be one tree_plan_upload made
+// from this plan, of at least the plan's device size.
+int check_dplan(const tree_plan_t* plan, const void* dplan, size_t dplan_bytes, const char* fn) {
+  const size_t need = plan->p.device_bytes();
+  if (dplan_bytes < need)
+    return fail(TREE_ERR_WORKSPACE, "%s: dplan has %zu bytes, the plan needs %zu", fn, dplan_bytes, need);
+  std::lock_guard<std::mutex> lock(plan->mu);
+  for (const auto& u : plan->uploads)
+    if (u.first == dplan) {
+      if (dplan_bytes > u.second)
+        return fail(TREE_ERR_INVALID_ARG, "%s: dplan_bytes %zu exceeds the %zu bytes it was uploaded with", fn,
+                    dplan_bytes, u.second);
+      return TREE_OK;
+    }
+  return fail(TREE_ERR_INVALID_ARG, "%s: dplan %p is not an upload of this plan (tree_plan_upload)", fn, dplan);
+}
 
 // Blocks along the tokens of the conv backward (each walks every n-th tile).
 int32_t conv_bwd_parts(const tg::Plan& p) {
@@ -124,12 +150,19 @@ int tree_plan_upload(const tree_plan_t* plan, void* dplan, size_t dplan_bytes, v
   const hipError_t e = hipMemcpyAsync(dplan, plan->p.mirror.data(), plan->p.device_bytes(),
                                       hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("tree_plan_upload: hipMemcpyAsync", e);
+  std::lock_guard<std::mutex> lock(plan->mu);
+  for (auto& u : plan->uploads)
+    if (u.first == dplan) {
+      u.second = dplan_bytes;
+      return TREE_OK;
+    }
+  plan->uploads.emplace_back(dplan, dplan_bytes);
   return TREE_OK;
 }
 
 int tree_conv(const void* x, const void* w, const void* bias, void* y, const void* init_ctx,
               void* ctx_out, int64_t n_tokens, int32_t channels, int32_t dtype, int32_t act,
-              const tree_plan_t* plan, const void* dplan, void* stream) {
+              const tree_plan_t* plan, const void* dplan, size_t dplan_bytes, void* stream) {
   if (!plan || !x || !w || !y || !dplan) return fail(TREE_ERR_INVALID_ARG, "tree_conv: null argument");
   const tg::Plan& p = plan->p;
   if (n_tokens != p.n_tokens)
@@ -143,6 +176,7 @@ int tree_conv(const void* x, const void* w, const void* bias, void* y, const voi
   if (x == y) return fail(TREE_ERR_INVALID_ARG, "tree_conv: y must not alias x");
   if (ctx_out != nullptr && (ctx_out == x || ctx_out == y || ctx_out == init_ctx))
     return fail(TREE_ERR_INVALID_ARG, "tree_conv: ctx_out must not alias x, y or init_ctx");
+  if (const int rc = check_dplan(plan, dplan, dplan_bytes, "tree_conv")) return rc;
   const int32_t* base = static_cast<const int32_t*>(dplan);
   tg::ConvArgs a{x, w, bias, y, static_cast<int32_t>(n_tokens), channels, p.width, dtype, act,
                  base + p.m_seg_off, base + p.m_hist, p.n_seg, init_ctx, ctx_out, base + p.m_ctx};
@@ -161,8 +195,8 @@ size_t tree_conv_backward_workspace_bytes(const tree_plan_t* plan, int32_t chann
 
 int tree_conv_backward(const void* x, const void* w, const void* bias, const void* dy, const void* init_ctx,
                        void* dx, float* dw, float* dbias, float* dinit_ctx, int64_t n_tokens, int32_t channels,
-                       int32_t dtype, int32_t act, const tree_plan_t* plan, const void* dplan, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       int32_t dtype, int32_t act, const tree_plan_t* plan, const void* dplan,
+                       size_t dplan_bytes, void* ws, size_t ws_bytes, void* stream) {
   if (!plan || !x || !w || !dy || !dx || !dw || !dplan)
     return fail(TREE_ERR_INVALID_ARG, "tree_conv_backward: null argument");
   const tg::Plan& p = plan->p;
@@ -179,6 +213,7 @@ int tree_conv_backward(const void* x, const void* w, const void* bias, const voi
   if (!ws || ws_bytes < need)
     return fail(TREE_ERR_WORKSPACE, "tree_conv_backward: workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0,
                 need);
+  if (const int rc = check_dplan(plan, dplan, dplan_bytes, "tree_conv_backward")) return rc;
   const int32_t* base = static_cast<const int32_t*>(dplan);
   tg::ConvBwdArgs a{};
   a.x = x;
@@ -218,10 +253,18 @@ size_t tree_scan_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d
   return static_cast<size_t>(plan->p.n_parents) * h_v * d_k * d_v * sizeof(float);
 }
 
+size_t tree_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d_k, int32_t d_v, int32_t sched) {
+  if (!plan) return 0;
+  if (sched == TREE_SCHED_AUTO) sched = tg::choose_schedule(plan->p, TREE_FORK_MIN_SAVED_TOKENS);
+  if (sched != TREE_SCHED_LEVEL) return 0;
+  return tree_scan_workspace_bytes(plan, h_v, d_k, d_v, 0);
+}
+
 int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,
                   void* o, const float* init_states, float* states, int64_t n_tokens, int32_t h_qk,
                   int32_t h_v, int32_t d_k, int32_t d_v, float scale, int32_t dtype, int32_t sched,
-                  const tree_plan_t* plan, const void* dplan, void* ws, size_t ws_bytes, void* stream) {
+                  const tree_plan_t* plan, const void* dplan, size_t dplan_bytes, void* ws, size_t ws_bytes,
+                  void* stream) {
   if (!plan || !q || !k || !v || !g || !beta || !o || !dplan)
     return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: null argument");
   const tg::Plan& p = plan->p;
@@ -247,6 +290,7 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, c
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(TREE_ERR_WORKSPACE, "tree_gdn_scan: workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0,
                 need);
+  if (const int rc = check_dplan(plan, dplan, dplan_bytes, "tree_gdn_scan")) return rc;
   const int32_t* base = static_cast<const int32_t*>(dplan);
   tg::ScanArgs a{};
   a.q = q;
@@ -299,7 +343,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
                            const float* states, float* dq, float* dk, float* dv, float* dg, float* dbeta,
                            float* dinit_states, int64_t n_tokens, int32_t h_qk, int32_t h_v, int32_t d_k,
                            int32_t d_v, float scale, int32_t dtype, const tree_plan_t* plan, const void* dplan,
-                           void* ws, size_t ws_bytes, void* stream) {
+                           size_t dplan_bytes, void* ws, size_t ws_bytes, void* stream) {
   if (!plan || !q || !k || !v || !g || !beta || !dout || !states || !dq || !dk || !dv || !dg || !dbeta || !dplan)
     return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan_backward: null argument");
   const tg::Plan& p = plan->p;
@@ -318,6 +362,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   if (!ws || ws_bytes < need)
     return fail(TREE_ERR_WORKSPACE, "tree_gdn_scan_backward: workspace has %zu bytes, needs %zu",
                 ws ? ws_bytes : 0, need);
+  if (const int rc = check_dplan(plan, dplan, dplan_bytes, "tree_gdn_scan_backward")) return rc;
   const int32_t* base = static_cast<const int32_t*>(dplan);
   const size_t dd = static_cast<size_t>(d_k) * d_v;
   tg::ScanBwdArgs a{};
@@ -383,7 +428,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
 int tree_ssd_scan(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
                   void* y, const float* init_states, float* states, int64_t n_tokens, int32_t n_groups,
                   int32_t n_heads, int32_t d_state, int32_t head_dim, int32_t dtype, const tree_plan_t* plan,
-                  const void* dplan, void* ws, size_t ws_bytes, void* stream) {
+                  const void* dplan, size_t dplan_bytes, void* ws, size_t ws_bytes, void* stream) {
   if (!plan || !x || !dt || !A || !B || !C || !y || !dplan)
     return fail(TREE_ERR_INVALID_ARG, "tree_ssd_scan: null argument");
   const tg::Plan& p = plan->p;
@@ -401,6 +446,7 @@ int tree_ssd_scan(const void* x, const float* dt, const float* A, const void* B,
   const size_t need = tree_scan_workspace_bytes(plan, n_heads, d_state, head_dim, states != nullptr);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(TREE_ERR_WORKSPACE, "tree_ssd_scan: workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0, need);
+  if (const int rc = check_dplan(plan, dplan, dplan_bytes, "tree_ssd_scan")) return rc;
   const int32_t* base = static_cast<const int32_t*>(dplan);
   tg::SsdArgs a{};
   a.x = x;

@@ -1,8 +1,8 @@
 // Host-side trie plan (no HIP headers: this file and plan.cpp build and run
 // without a GPU).
 //
-// The plan is what "TreePlan is built once per forward on the host" means on
-// the tree-recurrence 0.1.0 project page ("How a tree runs"): segment
+// The tree-recurrence 0.1.0 project page ("How a tree runs") makes one such
+// plan on the host per forward pass and runs every kernel on it: segment
 // offsets, the level schedule that lets every segment start from its
 // parent's final state ("Tree Training" section 3.2, Eq. 10: parents precede
 // children), and the conv history table that gives each segment the last

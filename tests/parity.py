@@ -1,14 +1,17 @@
 """Helpers shared by the GPU parity tests and the smoke check.
 
 The bar (fp64 oracle on the same bf16/fp32 inputs):
-  * outputs (o, y): max abs error <= 2e-2 beyond the rounding of the output
-    format itself, i.e. |out - ref| <= 2e-2 + half an ulp of the output dtype
-    at |ref| (bf16 spacing is 0.0625 for |ref| in [8, 16), so even the exactly
-    rounded answer can sit 0.031 from the reference there);
+  * outputs (o, y): max abs error |out - ref| <= 2e-2 wherever a correctly
+    rounded bf16 output can meet it, i.e. where half a bf16 ulp at |ref| is
+    below 2e-2 (|ref| < 8).  From |ref| = 8 on the bf16 spacing is 0.0625 or
+    more, so even the exactly rounded answer can sit 0.031 or more from the
+    reference; there the bar is 2e-2 beyond that half ulp;
   * segment final states: per (segment, value head), max-norm relative error
     max|S_gpu - S_ref| / max|S_ref| <= 1e-4.
 """
 from __future__ import annotations
+
+import sys
 
 import numpy as np
 
@@ -44,15 +47,37 @@ def half_ulp(ref, torch_dtype):
     return np.where(a > 0, np.exp2(e - 8), 0.0)
 
 
-def out_err(gpu_t, ref, rows=None, cols=None):
-    """Max over elements of |gpu - ref| - half_ulp(ref): the output error beyond
-    the output format's own rounding."""
+def rounding_allowance(ref, torch_dtype):
+    """What the output bar allows beyond 2e-2 at |ref|: half a bf16 ulp where
+    that alone exceeds 2e-2 (|ref| >= 8), zero elsewhere and for fp32."""
+    hu = half_ulp(ref, torch_dtype)
+    return np.where(hu >= OUT_ATOL, hu, 0.0)
+
+
+def out_errs(gpu_t, ref, rows=None, cols=None):
+    """Output errors of gpu_t against ref: a dict with the raw max abs error,
+    the max error beyond the output format's own rounding (|gpu - ref| -
+    half_ulp) and the asserted measure (|gpu - ref| - rounding_allowance),
+    which the bar holds to OUT_ATOL."""
     g = to_np(gpu_t)
     if rows is not None:
         g = g[rows]
     if cols is not None:
         g = g[..., cols] if g.ndim == 2 else g[:, cols]
-    return float((np.abs(g - ref) - half_ulp(ref, gpu_t.dtype)).max())
+    d = np.abs(g - ref)
+    return {"raw": float(d.max()),
+            "beyond_rounding": float((d - half_ulp(ref, gpu_t.dtype)).max()),
+            "asserted": float((d - rounding_allowance(ref, gpu_t.dtype)).max())}
+
+
+def out_err(gpu_t, ref, rows=None, cols=None, log=True):
+    """The asserted output error (see out_errs); the raw and beyond-rounding
+    figures are printed to stderr."""
+    e = out_errs(gpu_t, ref, rows, cols)
+    if log:
+        print(f"    output error: raw max abs {e['raw']:.3e}, beyond bf16 rounding {e['beyond_rounding']:.3e}, "
+              f"asserted {e['asserted']:.3e}", file=sys.stderr, flush=True)
+    return e["asserted"]
 
 
 def state_rel_err(s_gpu, s_ref):
@@ -91,22 +116,82 @@ def scan_errors_full(parents, lens, q, k, v, g, beta, o_gpu, st_gpu, scale=1.0, 
     return out_err(o_gpu, o_ref[:, hs], cols=hs), float(state_rel_err(sg, s_ref[:, hs]).max())
 
 
-def scan_errors_sampled(parents, lens, q, k, v, g, beta, o_gpu, st_gpu, segments, heads, scale=1.0):
-    """For each sampled segment, run the oracle over its root path for the given
-    value heads only; compare the rows and states of every segment on the path."""
+def _gdn_path_task(a):
+    """One oracle run (a process-pool task): a path's inputs for a block of
+    value heads (and their query/key heads) -> (outputs, end-of-segment states)."""
+    q, k, v, g, beta, scale, ends = a
+    return ogdn.gdn_on_path(q, k, v, g, beta, scale, snap_at=ends)
+
+
+def oracle_workers():
+    """Worker processes for the pooled oracle: the CPUs this process may use,
+    at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def run_pooled(fn, tasks, workers=None, timeout_s=600):
+    """[fn(t) for t in tasks] in a pool of fresh (spawned) interpreters that
+    import nothing but the oracle; one task runs in this process.  The pool
+    is terminated on any failure or after timeout_s, so a worker that cannot
+    start ends the call with an error rather than a wait."""
+    if len(tasks) <= 1:
+        return [fn(t) for t in tasks]
+    import multiprocessing as mp
+    pool = mp.get_context("spawn").Pool(min(len(tasks), workers or oracle_workers()))
+    try:
+        return pool.map_async(fn, tasks, chunksize=1).get(timeout_s)
+    finally:
+        pool.terminate()
+        pool.join()
+
+
+def scan_errors_sampled(parents, lens, q, k, v, g, beta, o_gpu, st_gpu, segments, heads=None, scale=1.0,
+                        workers=None):
+    """For each sampled segment, run the oracle over its root path and compare
+    the rows and final states of every segment on the path.  heads=None
+    checks every value head: the oracle runs in a spawned process pool, one
+    task per (segment, block of value heads sharing query/key heads).
+    Returns (asserted output error, max state rel error)."""
     import torch
-    worst_o, worst_s = 0.0, 0.0
+
+    h_qk, h_v = q.shape[1], v.shape[1]
+    grp = h_v // h_qk
+    if heads is None:
+        n_blk = min(h_qk, max(1, (workers or oracle_workers()) // max(1, len(segments))))
+        while h_qk % n_blk:
+            n_blk -= 1
+        qb = h_qk // n_blk
+        blocks = [np.arange(b * qb * grp, (b + 1) * qb * grp) for b in range(n_blk)]
+    else:
+        blocks = [np.asarray([h]) for h in heads]
+    tasks, meta = [], []
     for s in segments:
         path = otrie.root_path(parents, s)
         idx = torch.as_tensor(otrie.path_token_index(path, lens), device=q.device)
-        sel = lambda t: to_np(t.index_select(0, idx))  # noqa: E731
         ends = np.cumsum([int(lens[p]) for p in path]) - 1
-        op, snaps = ogdn.gdn_on_path(sel(q), sel(k), sel(v), sel(g), sel(beta), scale,
-                                     snap_at=ends, heads=heads)
-        worst_o = max(worst_o, out_err(o_gpu.index_select(0, idx), op, cols=heads))
-        for p, e in zip(path, ends):
-            sg = to_np(st_gpu[p])[heads]
-            worst_s = max(worst_s, float(state_rel_err(sg, snaps[int(e)]).max()))
+        host = {n: to_np(t.index_select(0, idx)) for n, t in (("q", q), ("k", k), ("v", v), ("g", g),
+                                                               ("beta", beta))}
+        for hs in blocks:
+            # A block is one value head or whole query/key groups, so inside
+            # the task value head j uses sliced query/key head j // (its group).
+            qh = np.unique(hs // grp)
+            tasks.append((host["q"][:, qh], host["k"][:, qh], host["v"][:, hs], host["g"][:, hs],
+                          host["beta"][:, hs], scale, ends))
+            meta.append((path, idx, ends, hs))
+    results = run_pooled(_gdn_path_task, tasks, workers)
+    worst_o, worst_s = 0.0, 0.0
+    raw = 0.0
+    for (path, idx, ends, hs), (op, snaps) in zip(meta, results):
+        e = out_errs(o_gpu.index_select(0, idx), op, cols=hs)
+        worst_o = max(worst_o, e["asserted"])
+        raw = max(raw, e["raw"])
+        for p, en in zip(path, ends):
+            sg = to_np(st_gpu[p])[hs]
+            worst_s = max(worst_s, float(state_rel_err(sg, snaps[int(en)]).max()))
+    print(f"    sampled scan check: {len(segments)} segments x {sum(len(b) for b in blocks)} value heads, "
+          f"output raw max abs {raw:.3e}, asserted {worst_o:.3e}, state rel {worst_s:.3e}",
+          file=sys.stderr, flush=True)
     return worst_o, worst_s
 
 

@@ -133,22 +133,80 @@ def test_argument_errors_need_no_device():
     plan = _lib.TreePlan(p, n, 4)
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     # token count mismatch
-    assert lib.tree_conv(fake, fake, None, fake, None, None, 6, 8, 1, 0, plan.handle, fake, None) == -3
+    big = 1 << 20
+    assert lib.tree_conv(fake, fake, None, fake, None, None, 6, 8, 1, 0, plan.handle, fake, big, None) == -3
     # bad activation / dtype
-    assert lib.tree_conv(fake, fake, None, fake, None, None, 5, 8, 1, 7, plan.handle, fake, None) == -1
-    assert lib.tree_conv(fake, fake, None, fake, None, None, 5, 8, 5, 0, plan.handle, fake, None) == -1
-    assert lib.tree_conv(fake, fake, None, fake, None, None, 5, 8, 1, 0, plan.handle, None, None) == -1
+    assert lib.tree_conv(fake, fake, None, fake, None, None, 5, 8, 1, 7, plan.handle, fake, big, None) == -1
+    assert lib.tree_conv(fake, fake, None, fake, None, None, 5, 8, 5, 0, plan.handle, fake, big, None) == -1
+    assert lib.tree_conv(fake, fake, None, fake, None, None, 5, 8, 1, 0, plan.handle, None, big, None) == -1
     # context out aliasing an input
     assert lib.tree_conv(fake, fake, None, ctypes.c_void_p(0x2000), None, fake, 5, 8, 1, 0, plan.handle,
-                         fake, None) == -1
+                         fake, big, None) == -1
     scan = lib.tree_gdn_scan
     args = [fake] * 6 + [None, fake]  # q, k, v, g, beta, o, init_states, states
-    assert scan(*args, 5, 2, 3, 128, 128, 1.0, 1, 0, plan.handle, fake, fake, 1 << 30, None) == -4
-    assert scan(*args, 5, 1, 1, 64, 64, 1.0, 1, 0, plan.handle, fake, fake, 1 << 30, None) == -4
-    assert scan(*args, 5, 1, 1, 128, 128, 1.0, 0, 0, plan.handle, fake, fake, 1 << 30, None) == -4
-    assert scan(*args, 4, 1, 1, 128, 128, 1.0, 1, 0, plan.handle, fake, fake, 1 << 30, None) == -3
-    assert scan(*args, 5, 1, 1, 128, 128, 1.0, 1, 9, plan.handle, fake, fake, 1 << 30, None) == -1
+    assert scan(*args, 5, 2, 3, 128, 128, 1.0, 1, 0, plan.handle, fake, big, fake, 1 << 30, None) == -4
+    assert scan(*args, 5, 1, 1, 64, 64, 1.0, 1, 0, plan.handle, fake, big, fake, 1 << 30, None) == -4
+    assert scan(*args, 5, 1, 1, 128, 128, 1.0, 0, 0, plan.handle, fake, big, fake, 1 << 30, None) == -4
+    assert scan(*args, 4, 1, 1, 128, 128, 1.0, 1, 0, plan.handle, fake, big, fake, 1 << 30, None) == -3
+    assert scan(*args, 5, 1, 1, 128, 128, 1.0, 1, 9, plan.handle, fake, big, fake, 1 << 30, None) == -1
     assert b"schedule" in lib.tree_last_error()
+
+
+def test_device_plan_must_be_an_upload_of_this_plan():
+    """Every entry point rejects, before any launch, a device plan whose byte
+    count is below the plan's device size (WORKSPACE) and one that
+    tree_plan_upload never filled from this plan (INVALID_ARG), with every
+    other argument valid.  No upload can run without a GPU, so here every
+    pointer is unknown; the GPU tests cover accepted uploads and a buffer
+    uploaded from another plan."""
+    lib = _lib.load()
+    parents, lens, _ = make_trie(2)
+    plan = _lib.TreePlan(parents, lens, 4)
+    n = plan.n_tokens
+    dbytes = plan.device_bytes()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced
+    other, other2 = ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)  # outputs may not alias inputs
+    ws = 1 << 40
+    calls = {
+        "tree_conv": lambda b: lib.tree_conv(fake, fake, None, other, None, None, n, 64, 1, 0, plan.handle,
+                                             fake, b, None),
+        "tree_conv_backward": lambda b: lib.tree_conv_backward(fake, fake, None, other, None, other2, fake, None,
+                                                               None, n, 64, 1, 0, plan.handle, fake, b, fake,
+                                                               ws, None),
+        "tree_gdn_scan": lambda b: lib.tree_gdn_scan(*([fake] * 6), None, None, n, 16, 16, 128, 128, 1.0, 1, 0,
+                                                     plan.handle, fake, b, fake, ws, None),
+        "tree_gdn_scan_backward": lambda b: lib.tree_gdn_scan_backward(
+            *([fake] * 6), None, None, fake, *([fake] * 5), None, n, 16, 16, 128, 128, 1.0, 1, plan.handle, fake,
+            b, fake, ws, None),
+        "tree_ssd_scan": lambda b: lib.tree_ssd_scan(fake, fake, fake, fake, fake, None, fake, None, None, n, 1, 8,
+                                                     128, 64, 1, plan.handle, fake, b, fake, ws, None),
+    }
+    for name, call in calls.items():
+        assert call(dbytes - 1) == -5, name
+        assert b"dplan" in lib.tree_last_error(), name
+        assert call(dbytes) == -1, name
+        assert b"not an upload of this plan" in lib.tree_last_error(), name
+    assert lib.tree_plan_upload(plan.handle, fake, dbytes - 1, None) == -5
+
+
+def test_tree_workspace_bytes_per_schedule():
+    """tree_workspace_bytes(plan, h_v, d_k, d_v, sched): the parent state
+    slots under the level schedule, nothing under rescan, auto resolved by
+    the fork/rescan policy."""
+    lib = _lib.load()
+    for cid in (2, 5):
+        parents, lens, _ = make_trie(cid)
+        plan = _lib.TreePlan(parents, lens, 4)
+        slots = plan.stats["n_parents"] * 32 * 128 * 128 * 4
+        assert lib.tree_workspace_bytes(plan.handle, 32, 128, 128, _lib.SCHED_LEVEL) == slots
+        assert lib.tree_workspace_bytes(plan.handle, 32, 128, 128, _lib.SCHED_RESCAN) == 0
+        auto = slots if plan.choose_schedule() == "level" else 0
+        assert lib.tree_workspace_bytes(plan.handle, 32, 128, 128, _lib.SCHED_AUTO) == auto
+    chain = _lib.TreePlan([-1, 0, 1], [10, 10, 10], 4)
+    assert chain.choose_schedule() == "rescan"
+    assert lib.tree_workspace_bytes(chain.handle, 4, 32, 32, _lib.SCHED_AUTO) == 0
+    assert lib.tree_workspace_bytes(chain.handle, 4, 32, 32, _lib.SCHED_LEVEL) == 2 * 4 * 32 * 32 * 4
+    assert lib.tree_workspace_bytes(None, 4, 32, 32, _lib.SCHED_LEVEL) == 0
 
 
 def test_workspace_size_and_check():
@@ -161,7 +219,7 @@ def test_workspace_size_and_check():
     fake = ctypes.c_void_p(0x1000)
     n = plan.n_tokens
     rc = lib.tree_gdn_scan(*([fake] * 6), None, None, n, 16, 16, 128, 128, 1.0, 1, 0, plan.handle, fake,
-                           fake, need - 1, None)
+                           1 << 20, fake, need - 1, None)
     assert rc == -5
 
 
@@ -273,7 +331,7 @@ def test_scan_backward_workspace_size_and_checks(cid):
 
     def call(n_tok=n, h_qk=s.h_qk, h_v=s.h_v, d=s.d_k, dtype=dt, ws=need, states=fake):
         return bwd(*([fake] * 6), None, None, states, *([fake] * 5), None, n_tok, h_qk, h_v, d, d, 1.0, dtype,
-                   plan.handle, fake, fake, ws, None)
+                   plan.handle, fake, 1 << 20, fake, ws, None)
 
     assert call(ws=need - 1) == -5
     assert call(n_tok=n + 1) == -3
@@ -296,7 +354,7 @@ def test_ssd_scan_argument_checks_need_no_device():
 
     def call(n_tok=n, groups=1, heads=8, d_state=128, head_dim=64, dtype=1, ws=need, states=None, x=fake):
         return lib.tree_ssd_scan(x, fake, fake, fake, fake, None, fake, None, states, n_tok, groups, heads, d_state,
-                                 head_dim, dtype, plan.handle, fake, fake, ws, None)
+                                 head_dim, dtype, plan.handle, fake, 1 << 20, fake, ws, None)
 
     assert call(n_tok=n - 1) == -3
     assert call(groups=3) == -4
