@@ -71,7 +71,7 @@ def test_device_plan_identity_checked_on_the_host():
     say("device plan identity")
     lib = _lib.load()
     plan = ptp.tree_plan(PARENTS, LENS, 4)
-    other = ptp.tree_plan(np.array([-1, 0, 1, 1], np.int32), LENS, 4)
+    other = ptp.tree_plan(PARENTS, np.array([40, 9, 17, 33], np.int32), 4)  # same size, other rows
     assert plan.device_bytes() == other.device_bytes()
     c = make_conv_inputs(N, 64, 4, "bf16", DEV, seed=4)
     y = torch.empty_like(c["x"])
