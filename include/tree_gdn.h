@@ -329,6 +329,34 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g,
                   int32_t sched, const tree_plan_t* plan, const void* dplan, size_t dplan_bytes,
                   void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the static device scratch array behind tree_gdn_scan_noalloc (one
+ * per GPU the library runs on, held until the process ends). */
+#define TREE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * tree_gdn_scan_noalloc -- tree_gdn_scan for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * tree_gdn_scan, without dplan and ws: the device plan and the parent-state
+ * slots live in a library-owned static device array of
+ * TREE_NOALLOC_SCRATCH_BYTES on each GPU.  The call copies the plan into it
+ * (an asynchronous host-to-device copy on `stream`; the plan must stay alive
+ * until the stream has run it) and launches the same kernels as
+ * tree_gdn_scan; it calls no hipMalloc, hipFree or other allocating routine.
+ * Needs tree_plan_device_bytes(plan), rounded up to 256, plus
+ * tree_scan_workspace_bytes(plan, h_v, d_k, d_v, states != NULL) under the
+ * level schedule (nothing under rescan) to fit in the array; a larger call is
+ * rejected with TREE_ERR_WORKSPACE before any device work.  `stream` must
+ * belong to the calling thread's current device.  Every call on a GPU shares
+ * that GPU's array and leaves its contents behind: calls that overlap on one
+ * GPU (different streams, or several threads) race and must be serialised
+ * by the caller; calls on one stream are ordered by it.
+ */
+int tree_gdn_scan_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta, void* o,
+                          const float* init_states, float* states, int64_t n_tokens, int32_t h_qk, int32_t h_v,
+                          int32_t d_k, int32_t d_v, float scale, int32_t dtype, int32_t sched,
+                          const tree_plan_t* plan, void* stream);
+
 /*
  * tree_gdn_scan_backward_workspace_bytes -- device workspace
  * tree_gdn_scan_backward needs: the start state ([h_v, d_k, d_v] fp32) and

@@ -69,6 +69,8 @@ SIGNATURES = {
     "tree_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
     "tree_gdn_scan": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
                                      _F, _I32, _I32, _P, _P, _SZ, _P, _SZ, _P]),
+    "tree_gdn_scan_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
+                                             _F, _I32, _I32, _P, _P]),
     "tree_gdn_scan_backward_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
     "tree_gdn_scan_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                               _I32, _I32, _I32, _I32, _F, _I32, _P, _P, _SZ, _P, _SZ, _P]),

@@ -260,38 +260,43 @@ size_t tree_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d_k, i
   return tree_scan_workspace_bytes(plan, h_v, d_k, d_v, 0);
 }
 
-int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,
-                  void* o, const float* init_states, float* states, int64_t n_tokens, int32_t h_qk,
-                  int32_t h_v, int32_t d_k, int32_t d_v, float scale, int32_t dtype, int32_t sched,
-                  const tree_plan_t* plan, const void* dplan, size_t dplan_bytes, void* ws, size_t ws_bytes,
-                  void* stream) {
-  if (!plan || !q || !k || !v || !g || !beta || !o || !dplan)
-    return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: null argument");
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by tree_gdn_scan and tree_gdn_scan_noalloc (all but
+// the device plan and the workspace).  Resolves AUTO into *sched and returns
+// in *need the parent-slot bytes the level schedule needs.
+int check_scan(const char* fn, const void* q, const void* k, const void* v, const float* g, const float* beta,
+               void* o, const float* states, int64_t n_tokens, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+               int32_t dtype, int32_t* sched, const tree_plan_t* plan, size_t* need) {
+  if (!plan || !q || !k || !v || !g || !beta || !o) return fail(TREE_ERR_INVALID_ARG, "%s: null argument", fn);
   const tg::Plan& p = plan->p;
   if (n_tokens != p.n_tokens)
-    return fail(TREE_ERR_SIZE, "tree_gdn_scan: n_tokens %lld != plan tokens %lld",
-                static_cast<long long>(n_tokens), static_cast<long long>(p.n_tokens));
+    return fail(TREE_ERR_SIZE, "%s: n_tokens %lld != plan tokens %lld", fn, static_cast<long long>(n_tokens),
+                static_cast<long long>(p.n_tokens));
   if (h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0)
-    return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: head counts and sizes must be > 0");
+    return fail(TREE_ERR_INVALID_ARG, "%s: head counts and sizes must be > 0", fn);
   if (h_v % h_qk != 0)
-    return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan: h_v %d is not a multiple of h_qk %d", h_v, h_qk);
-  if (!dtype_ok(dtype)) return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: bad dtype %d", dtype);
-  if (sched == TREE_SCHED_AUTO) sched = tg::choose_schedule(p, TREE_FORK_MIN_SAVED_TOKENS);
-  if (sched != TREE_SCHED_LEVEL && sched != TREE_SCHED_RESCAN)
-    return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: bad schedule %d", sched);
-  if (sched == TREE_SCHED_RESCAN && !p.paths_ok)
-    return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan: rescan walk table of %lld entries not built",
+    return fail(TREE_ERR_UNSUPPORTED, "%s: h_v %d is not a multiple of h_qk %d", fn, h_v, h_qk);
+  if (!dtype_ok(dtype)) return fail(TREE_ERR_INVALID_ARG, "%s: bad dtype %d", fn, dtype);
+  if (*sched == TREE_SCHED_AUTO) *sched = tg::choose_schedule(p, TREE_FORK_MIN_SAVED_TOKENS);
+  if (*sched != TREE_SCHED_LEVEL && *sched != TREE_SCHED_RESCAN)
+    return fail(TREE_ERR_INVALID_ARG, "%s: bad schedule %d", fn, *sched);
+  if (*sched == TREE_SCHED_RESCAN && !p.paths_ok)
+    return fail(TREE_ERR_UNSUPPORTED, "%s: rescan walk table of %lld entries not built", fn,
                 static_cast<long long>(p.path_entries));
   if (!tg::scan_supported(d_k, d_v, dtype))
-    return fail(TREE_ERR_UNSUPPORTED, "tree_gdn_scan: d_k=%d d_v=%d dtype=%d not compiled in", d_k,
-                d_v, dtype);
-  const size_t need =
-      sched == TREE_SCHED_LEVEL ? tree_scan_workspace_bytes(plan, h_v, d_k, d_v, states != nullptr) : 0;
-  if (need > 0 && (!ws || ws_bytes < need))
-    return fail(TREE_ERR_WORKSPACE, "tree_gdn_scan: workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0,
-                need);
-  if (const int rc = check_dplan(plan, dplan, dplan_bytes, "tree_gdn_scan")) return rc;
-  const int32_t* base = static_cast<const int32_t*>(dplan);
+    return fail(TREE_ERR_UNSUPPORTED, "%s: d_k=%d d_v=%d dtype=%d not compiled in", fn, d_k, d_v, dtype);
+  *need = *sched == TREE_SCHED_LEVEL ? tree_scan_workspace_bytes(plan, h_v, d_k, d_v, states != nullptr) : 0;
+  return TREE_OK;
+}
+
+// The scan's launches on a device plan `base` and parent-state slots `slots`.
+int launch_scan_levels(const char* fn, const void* q, const void* k, const void* v, const float* g,
+                       const float* beta, void* o, const float* init_states, float* states, int32_t h_qk,
+                       int32_t h_v, int32_t d_k, int32_t d_v, float scale, int32_t dtype, int32_t sched,
+                       const tg::Plan& p, const int32_t* base, float* slots, hipStream_t st) {
   tg::ScanArgs a{};
   a.q = q;
   a.k = k;
@@ -302,29 +307,108 @@ int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, c
   a.init = init_states;
   a.root_idx = base + p.m_root;
   a.states = states;
-  a.slots = static_cast<float*>(ws);
+  a.slots = slots;
   a.seg_off = base + p.m_seg_off;
   a.parent = base + p.m_parent;
   a.slot = base + p.m_slot;
   a.h_qk = h_qk;
   a.h_v = h_v;
   a.scale = scale;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
   if (sched == TREE_SCHED_RESCAN) {
     a.walk_off = base + p.m_path_off;
     a.walk = base + p.m_path_seg;
     a.n_items = p.n_leaves;
     const hipError_t e = tg::launch_scan(a, d_k, d_v, dtype, true, st);
-    if (e != hipSuccess) return hip_fail("tree_gdn_scan: launch", e);
+    if (e != hipSuccess) return hip_fail(fn, e);
     return TREE_OK;
   }
   for (int32_t l = 0; l < p.n_levels; ++l) {
     a.items = base + p.m_order + p.level_start[l];
     a.n_items = p.level_start[l + 1] - p.level_start[l];
     const hipError_t e = tg::launch_scan(a, d_k, d_v, dtype, false, st);
-    if (e != hipSuccess) return hip_fail("tree_gdn_scan: launch", e);
+    if (e != hipSuccess) return hip_fail(fn, e);
   }
   return TREE_OK;
+}
+
+// Device scratch of tree_gdn_scan_noalloc: the device plan at offset 0, the
+// parent-state slots from the next 256-byte boundary.  Each GPU holds its own
+// copy for the life of the process.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[TREE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(const char* fn, unsigned char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(TREE_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (!ptr) return fail(TREE_ERR_HIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<unsigned char*>(g_scratch_ptr[dev]);
+  return TREE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tree_gdn_scan(const void* q, const void* k, const void* v, const float* g, const float* beta,
+                  void* o, const float* init_states, float* states, int64_t n_tokens, int32_t h_qk,
+                  int32_t h_v, int32_t d_k, int32_t d_v, float scale, int32_t dtype, int32_t sched,
+                  const tree_plan_t* plan, const void* dplan, size_t dplan_bytes, void* ws, size_t ws_bytes,
+                  void* stream) {
+  size_t need = 0;
+  if (const int rc = check_scan("tree_gdn_scan", q, k, v, g, beta, o, states, n_tokens, h_qk, h_v, d_k, d_v, dtype,
+                                &sched, plan, &need))
+    return rc;
+  if (!dplan) return fail(TREE_ERR_INVALID_ARG, "tree_gdn_scan: null argument");
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(TREE_ERR_WORKSPACE, "tree_gdn_scan: workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0,
+                need);
+  if (const int rc = check_dplan(plan, dplan, dplan_bytes, "tree_gdn_scan")) return rc;
+  return launch_scan_levels("tree_gdn_scan: launch", q, k, v, g, beta, o, init_states, states, h_qk, h_v, d_k, d_v,
+                            scale, dtype, sched, plan->p, static_cast<const int32_t*>(dplan),
+                            static_cast<float*>(ws), static_cast<hipStream_t>(stream));
+}
+
+int tree_gdn_scan_noalloc(const void* q, const void* k, const void* v, const float* g, const float* beta, void* o,
+                          const float* init_states, float* states, int64_t n_tokens, int32_t h_qk, int32_t h_v,
+                          int32_t d_k, int32_t d_v, float scale, int32_t dtype, int32_t sched,
+                          const tree_plan_t* plan, void* stream) {
+  const char* fn = "tree_gdn_scan_noalloc";
+  size_t need = 0;
+  if (const int rc = check_scan(fn, q, k, v, g, beta, o, states, n_tokens, h_qk, h_v, d_k, d_v, dtype, &sched,
+                                plan, &need))
+    return rc;
+  const size_t plan_bytes = plan->p.device_bytes();
+  const size_t slot_off = (plan_bytes + 255) / 256 * 256;
+  if (slot_off + need > TREE_NOALLOC_SCRATCH_BYTES)
+    return fail(TREE_ERR_WORKSPACE,
+                "%s: needs %zu bytes of scratch (device plan %zu + parent states %zu), the static maximum is %zu; "
+                "pass `states` (then no parent slots are needed) or use tree_gdn_scan with a workspace",
+                fn, slot_off + need, plan_bytes, need, static_cast<size_t>(TREE_NOALLOC_SCRATCH_BYTES));
+  unsigned char* ptr = nullptr;
+  if (const int rc = scratch_on_current_device(fn, &ptr)) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // The device plan goes into the scratch on the caller's stream, ahead of
+  // the launches that read it.  Nothing in the scratch needs clearing: every
+  // parent slot is written by its parent before a child reads it.
+  const hipError_t e = hipMemcpyAsync(ptr, plan->p.mirror.data(), plan_bytes, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail("tree_gdn_scan_noalloc: hipMemcpyAsync", e);
+  return launch_scan_levels("tree_gdn_scan_noalloc: launch", q, k, v, g, beta, o, init_states, states, h_qk, h_v,
+                            d_k, d_v, scale, dtype, sched, plan->p, reinterpret_cast<const int32_t*>(ptr),
+                            reinterpret_cast<float*>(ptr + slot_off), st);
 }
 
 size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h_qk, int32_t h_v, int32_t d_k,

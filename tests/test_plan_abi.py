@@ -374,3 +374,24 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         _lib.load()
     with pytest.raises(OSError, match="is missing"):
         _lib.tree_plan(np.array([-1, 0], np.int32), np.array([3, 2], np.int32), 4)
+
+
+def test_noalloc_scan_rejects_sizes_beyond_its_scratch_without_a_device():
+    """tree_gdn_scan_noalloc checks that the device plan and the parent slots
+    fit its static array before touching the device: the RL batch trie's 93
+    parent states of 32 heads (186 MiB) exceed TREE_NOALLOC_SCRATCH_BYTES."""
+    lib = _lib.load()
+    text = open(HEADER).read()
+    cap = re.search(r"#define TREE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    cap = int(cap.group(1)) << int(cap.group(2))
+    parents, lens, _ = make_trie(5)
+    plan = _lib.TreePlan(parents, lens, 4)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced
+    need = lib.tree_scan_workspace_bytes(plan.handle, 32, 128, 128, 0)
+    assert need + plan.device_bytes() > cap
+    rc = lib.tree_gdn_scan_noalloc(*([fake] * 6), None, None, plan.n_tokens, 16, 32, 128, 128, 1.0, 1,
+                                   _lib.SCHED_LEVEL, plan.handle, None)
+    assert rc == -5 and b"static maximum" in lib.tree_last_error()
+    # the usual argument checks come first
+    assert lib.tree_gdn_scan_noalloc(*([fake] * 6), None, None, plan.n_tokens + 1, 16, 32, 128, 128, 1.0, 1,
+                                     _lib.SCHED_LEVEL, plan.handle, None) == -3
