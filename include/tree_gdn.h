@@ -318,7 +318,7 @@ size_t tree_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d_k, i
  * dplan, dplan_bytes  as for tree_conv.
  * ws     device workspace of ws_bytes >= tree_scan_workspace_bytes (may be
  *        NULL under TREE_SCHED_RESCAN).
- * Compiled head sizes: d_k = d_v in {32, 128} for bf16, 32 for fp32.
+ * Compiled head sizes: d_k = d_v in {32, 64, 128} for bf16, {32, 64} for fp32.
  * Errors: INVALID_ARG, SIZE, UNSUPPORTED (also: RESCAN without a walk
  * table), WORKSPACE, HIP.
  */

@@ -641,15 +641,23 @@ hipError_t launch_one(const ScanArgs& a, bool paths, hipStream_t stream) {
 
 bool scan_supported(int d_k, int d_v, int dtype) {
   if (d_k != d_v) return false;
-  if (dtype == TREE_DTYPE_F32) return d_k == 32;
-  return d_k == 32 || d_k == 128;
+  if (dtype == TREE_DTYPE_F32) return d_k == 32 || d_k == 64;
+  return d_k == 32 || d_k == 64 || d_k == 128;
 }
 
 hipError_t launch_scan(const ScanArgs& a, int d_k, int d_v, int dtype, bool paths, hipStream_t stream) {
   const bool f32 = dtype == TREE_DTYPE_F32;
   if (d_k == 128 && d_v == 128 && !f32) return launch_scan_d128(a, paths, stream);
-  if (d_k == 32 && d_v == 32)
+  if (d_k == 64 && d_v == 64)
+    return f32 ? launch_one<64, 64, true, 1>(a, paths, stream) : launch_one<64, 64, false, 1>(a, paths, stream);
+  if (d_k == 32 && d_v == 32) {
+    // Value heads 2j and 2j + 1 share a query/key head when the group size
+    // h_v / h_qk is even: one work-group then serves both and stages their q
+    // and k once.
+    if ((a.h_v / a.h_qk) % 2 == 0)
+      return f32 ? launch_one<32, 32, true, 2>(a, paths, stream) : launch_one<32, 32, false, 2>(a, paths, stream);
     return f32 ? launch_one<32, 32, true, 1>(a, paths, stream) : launch_one<32, 32, false, 1>(a, paths, stream);
+  }
   return hipErrorInvalidValue;
 }
 

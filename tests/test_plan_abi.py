@@ -145,7 +145,8 @@ def test_argument_errors_need_no_device():
     scan = lib.tree_gdn_scan
     args = [fake] * 6 + [None, fake]  # q, k, v, g, beta, o, init_states, states
     assert scan(*args, 5, 2, 3, 128, 128, 1.0, 1, 0, plan.handle, fake, big, fake, 1 << 30, None) == -4
-    assert scan(*args, 5, 1, 1, 64, 64, 1.0, 1, 0, plan.handle, fake, big, fake, 1 << 30, None) == -4
+    assert scan(*args, 5, 1, 1, 48, 48, 1.0, 1, 0, plan.handle, fake, big, fake, 1 << 30, None) == -4
+    assert scan(*args, 5, 1, 1, 128, 128, 1.0, 0, 0, plan.handle, fake, big, fake, 1 << 30, None) == -4
     assert scan(*args, 5, 1, 1, 128, 128, 1.0, 0, 0, plan.handle, fake, big, fake, 1 << 30, None) == -4
     assert scan(*args, 4, 1, 1, 128, 128, 1.0, 1, 0, plan.handle, fake, big, fake, 1 << 30, None) == -3
     assert scan(*args, 5, 1, 1, 128, 128, 1.0, 1, 9, plan.handle, fake, big, fake, 1 << 30, None) == -1
