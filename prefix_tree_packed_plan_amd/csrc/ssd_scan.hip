@@ -46,6 +46,25 @@ struct SsdSmem {
   alignas(16) float y[L * P];   // the chunk's outputs, stored as whole rows after the chunk
 };
 
+// Block -> (item, head), XCD-aware.  Work-groups are dealt to the 8 XCDs in
+// turn (block b runs on XCD b % 8), and every head of a segment reads the
+// same B and C rows (one group, or a few, for all heads).  Within each run of
+// 8 items the blocks are ordered so that XCD x gets every head of item
+// 8 j + x, and the B/C rows of a segment are fetched into one XCD's L2 instead
+// of all eight.  Items past the last whole run of 8 keep the plain order.
+__device__ __forceinline__ void ssd_block_item(int b, int n_items, int n_heads, int& item, int& h) {
+  const int full = (n_items / 8) * 8;
+  if (b < full * n_heads) {
+    const int gi = b / (8 * n_heads), r = b - gi * 8 * n_heads;
+    item = 8 * gi + (r & 7);
+    h = r >> 3;
+  } else {
+    const int r = b - full * n_heads;
+    item = full + r / n_heads;
+    h = r - (r / n_heads) * n_heads;
+  }
+}
+
 template <int N, int P, bool F32IN>
 __global__ __launch_bounds__(4 * P, 2) void ssd_level_kernel(SsdArgs a) {
   constexpr int NT = N / 16;  // row tiles of the state
@@ -60,8 +79,8 @@ __global__ __launch_bounds__(4 * P, 2) void ssd_level_kernel(SsdArgs a) {
   const int i16 = lane & 15;
   const int col = 16 * w + i16;
 
-  const int item = blockIdx.x / a.n_heads;
-  const int h = blockIdx.x - item * a.n_heads;
+  int item, h;
+  ssd_block_item(blockIdx.x, a.n_items, a.n_heads, item, h);
   const int seg = a.items[item];
   const int grp = h / (a.n_heads / a.n_groups);
   const int par = a.parent[seg];
@@ -220,8 +239,8 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   const int col = 16 * w + i16;
   const uint2 negI = neg_identity(h4, i16);
 
-  const int item = blockIdx.x / a.n_heads;
-  const int h = blockIdx.x - item * a.n_heads;
+  int item, h;
+  ssd_block_item(blockIdx.x, a.n_items, a.n_heads, item, h);
   const int seg = a.items[item];
   const int grp = h / (a.n_heads / a.n_groups);
   const int par = a.parent[seg];
