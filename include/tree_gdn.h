@@ -359,10 +359,13 @@ int tree_gdn_scan_noalloc(const void* q, const void* k, const void* v, const flo
 
 /*
  * tree_gdn_scan_backward_workspace_bytes -- device workspace
- * tree_gdn_scan_backward needs: the start state ([h_v, d_k, d_v] fp32) and
- * three [h_v, 16, 16] fp32 matrices of every 16-token chunk, one
- * start-state gradient ([h_v, d_k, d_v] fp32) per segment, plus
- * per-value-head dq and dk
+ * tree_gdn_scan_backward needs: the start state ([h_v, d_k, d_v] fp32) of
+ * every 8th 16-token chunk of each segment (a checkpoint; the chunks between
+ * two checkpoints are re-run forward from it when the backward reaches
+ * them), three [h_v, 16, 16] fp32 matrices of every chunk, one start-state
+ * gradient ([h_v, d_k, d_v] fp32) per segment, room for 7 re-run start
+ * states per work-group of the largest trie level ([7, d_k, d_v] fp32 per
+ * segment of that level and value head), plus per-value-head dq and dk
  * ([n_tokens, h_v, d_k] fp32 each) when h_v > 2 h_qk.
  */
 size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h_qk, int32_t h_v, int32_t d_k,
@@ -380,7 +383,8 @@ size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h
  * accumulation); levels run from the deepest up.  The result is
  * deterministic.  Within a segment the chunked form is differentiated
  * chunk by chunk (16-token chunks, fp32 MFMA), each chunk's start state
- * recomputed from the parent's final state.
+ * recomputed from the parent's final state (every 8th stored, the others
+ * re-run from the last stored one).
  * q, k, v, g, beta, init_states, scale, dtype   as passed to tree_gdn_scan.
  * dout    device, [n_tokens, h_v, d_v], dtype        (read)
  * dstates device, [n_seg, h_v, d_k, d_v] fp32, or NULL (no gradient on the

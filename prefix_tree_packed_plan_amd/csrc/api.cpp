@@ -411,15 +411,43 @@ int tree_gdn_scan_noalloc(const void* q, const void* k, const void* v, const flo
                             reinterpret_cast<float*>(ptr + slot_off), st);
 }
 
+}  // extern "C"
+
+namespace {
+
+static_assert(tg::kBwdCkpt == tg::Plan::kBwdCkpt, "one checkpoint interval for the plan and the kernels");
+
+// Scan backward workspace, in floats, in this order: checkpoint states (slot
+// gck[s] + j for segment s's j-th),
+// one start-state gradient per segment, every chunk's T, KK and QK, the
+// level work-groups' re-run scratch (kBwdCkpt - 1 states each, for the
+// largest level), and per-value-head dq, dk when h_v > 2 h_qk.
+struct BwdLayout {
+  size_t ck, dsseg, tws, scr, per_head, total;
+};
+
+BwdLayout bwd_layout(const tg::Plan& p, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v) {
+  const size_t dd = static_cast<size_t>(d_k) * d_v;
+  int32_t max_level = 0;
+  for (int32_t l = 0; l < p.n_levels; ++l) max_level = std::max(max_level, p.level_start[l + 1] - p.level_start[l]);
+  BwdLayout b{};
+  b.ck = 0;
+  b.dsseg = b.ck + static_cast<size_t>(p.total_ckpts) * h_v * dd;
+  b.tws = b.dsseg + static_cast<size_t>(p.n_seg) * h_v * dd;
+  b.scr = b.tws + static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
+  b.per_head = b.scr + static_cast<size_t>(max_level) * h_v * (tg::kBwdCkpt - 1) * dd;
+  b.total = b.per_head + (h_v > 2 * h_qk ? 2 * static_cast<size_t>(p.n_tokens) * h_v * d_k : 0);
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h_qk, int32_t h_v, int32_t d_k,
                                               int32_t d_v) {
   if (!plan || h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0) return 0;
-  const tg::Plan& p = plan->p;
-  const size_t dd = static_cast<size_t>(d_k) * d_v;
-  size_t n = (static_cast<size_t>(p.total_chunks) + p.n_seg) * h_v * dd;
-  n += static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
-  if (h_v > 2 * h_qk) n += 2 * static_cast<size_t>(p.n_tokens) * h_v * d_k;  // per-value-head dq, dk
-  return n * sizeof(float);
+  return bwd_layout(plan->p, h_qk, h_v, d_k, d_v).total * sizeof(float);
 }
 
 int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const float* g, const float* beta,
@@ -463,10 +491,13 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.dg = dg;
   a.dbeta = dbeta;
   a.dinit = dinit_states;
-  a.hws = static_cast<float*>(ws);
-  a.dsseg = a.hws + static_cast<size_t>(p.total_chunks) * h_v * dd;
-  a.tws = a.dsseg + static_cast<size_t>(p.n_seg) * h_v * dd;
-  float* per_head = a.tws + static_cast<size_t>(p.total_chunks) * h_v * 3 * tg::Plan::kBwdChunk * tg::Plan::kBwdChunk;
+  const BwdLayout lay = bwd_layout(p, h_qk, h_v, d_k, d_v);
+  float* const wsf = static_cast<float*>(ws);
+  a.hws = wsf + lay.ck;
+  a.dsseg = wsf + lay.dsseg;
+  a.tws = wsf + lay.tws;
+  a.scr = wsf + lay.scr;
+  float* per_head = wsf + lay.per_head;
   // One value head per q/k head: dq, dk written directly.  Two: the prep
   // launch clears dq, dk and both heads add into them.  More: per-value-head
   // parts, summed in head order.
@@ -483,6 +514,7 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.kid = base + p.m_kid;
   a.gchunk = base + p.m_gchunk;
   a.chunk_seg = base + p.m_chunk_seg;
+  a.gck = base + p.m_gck;
   a.n_chunks = static_cast<int32_t>(p.total_chunks);
   a.n_seg = p.n_seg;
   a.h_qk = h_qk;

@@ -113,12 +113,60 @@ __device__ __forceinline__ void solve(const f32x4 kk, const Gates& s, int h4, in
   Tt = mm(N8, X3t, X3t);  // (X3 N8)^T = N8^T X3^T; N8^T's A operand is N8's tile
 }
 
-// Forward re-run: every chunk's start state, for all segments at once (a
-// segment starts from its parent's final state, which the forward already
-// wrote), into the workspace as 16x16 tiles (row tile rt, column tile ct at
-// (rt * NT + ct) * 256 floats), each in the lanes' accumulator order (lane
-// l's 4 values at 4l): one 16-byte store per lane and tile.  Few registers,
-// so two work-groups share a compute unit.
+// One chunk of the forward recurrence on a work-group's state: St (this
+// wave's 16 columns of S0, as row tiles) becomes S1 = gamma_last S0 +
+// K^T diag(delta) T diag(b) (V - diag(gamma) K S0).  sk, sg, sb: the chunk's
+// K rows (row stride D + 4), g and beta, staged in LDS; Tt: the lane's tile of
+// T^T; vc: the lane's V values (rows 4 h4 + 0..3 of its column), zero past
+// the segment end.  The states kernel and the level kernel's re-run of the
+// chunks after a checkpoint both step the state here, so the re-run start
+// states are bitwise the states kernel's.
+template <int D, bool F32IN>
+__device__ __forceinline__ void fwd_chunk_state(f32x4 (&St)[D / 16], const float* sk, const float* sg, const float* sb,
+                                                const f32x4 Tt, const f32x4 vc, const uint2 negI, int h4, int i16) {
+  constexpr int NT = D / 16;
+  constexpr int S = D + 4;
+  const Gates gt = make_gates(sg, sb, h4, i16);
+  f32x4 ks = z4();
+  if constexpr (F32IN) {
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) ks = mm(ld4(&sk[i16 * S + 16 * rt + 4 * h4]), St[rt], ks);
+  } else {
+#pragma unroll
+    for (int m = 0; m < NT / 2; ++m) {
+      const uint4 ak = exact8(&sk[i16 * S + 32 * m + 4 * h4]);
+      uint4 bh, bl;
+      split8m(St[2 * m], St[2 * m + 1], negI, bh, bl);
+      ks = mma32(ak, bl, mma32(ak, bh, ks));
+    }
+  }
+  f32x4 R;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) R[r] = gt.bet[r] * (vc[r] - gt.gam[r] * ks[r]);
+  const f32x4 U = mm(Tt, R, z4());
+  const f32x4 dU = gt.del * U;
+  uint2 uh, ul;
+  if constexpr (!F32IN) split4(dU, uh, ul);
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    f32x4 akt;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) akt[s] = sk[(4 * h4 + s) * S + 16 * rt + i16];
+    if constexpr (F32IN) {
+      St[rt] = mm(akt, dU, gt.gam_last * St[rt]);
+    } else {
+      const uint2 a = pack4(akt);
+      St[rt] = mma16b(a, ul, mma16b(a, uh, gt.gam_last * St[rt]));
+    }
+  }
+}
+
+// Forward re-run of the checkpoints: the start state of every kBwdCkpt-th
+// chunk, for all segments at once (a segment starts from its parent's final
+// state, which the forward already wrote), into the workspace as 16x16 tiles
+// (row tile rt, column tile ct at (rt * NT + ct) * 256 floats), each in the
+// lanes' accumulator order (lane l's 4 values at 4l): one 16-byte store per
+// lane and tile.  Few registers, so two work-groups share a compute unit.
 template <int D>
 struct StatesSmem {
   static constexpr int S = D + 4;
@@ -146,7 +194,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_states_kernel(ScanBwdArgs a)
   const int nc = (t_end - t_beg + L - 1) / L;
   const size_t DD = size_t(D) * D;
   const size_t cstride = size_t(a.h_v) * DD;
-  float* hws = a.hws + (size_t(a.gchunk[seg]) * a.h_v + h) * DD;
+  // Checkpoints: the start state of every kBwdCkpt-th chunk of the segment.
+  float* hws = a.hws + (size_t(a.gck[seg]) * a.h_v + h) * DD;
   constexpr int TW = 3 * L * L;
   const size_t tstride = size_t(a.h_v) * TW;
   const float* tws = a.tws + (size_t(a.gchunk[seg]) * a.h_v + h) * TW;
@@ -205,8 +254,11 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_states_kernel(ScanBwdArgs a)
       }
     };
     fetch(0);
-    for (int c = 0; c < nc; ++c) {
-      store_ws(hws + c * cstride, St);
+    // The chunks after the last checkpoint are re-run by the level kernel.
+    const int c_last = ((nc - 1) / kBwdCkpt) * kBwdCkpt;
+    for (int c = 0; c <= c_last; ++c) {
+      if (c % kBwdCkpt == 0) store_ws(hws + (c / kBwdCkpt) * cstride, St);
+      if (c == c_last) break;
       f32x4 kv, vc;
       if constexpr (F32IN) {
         kv = kraw;
@@ -230,39 +282,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_states_kernel(ScanBwdArgs a)
       const f32x4 Tt = Ttn;
       __syncthreads();
       if (c + 1 < nc) fetch(c + 1);
-      const Gates gt = make_gates(sm.g, sm.b, h4, i16);
-      f32x4 ks = z4();
-      if constexpr (F32IN) {
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) ks = mm(ld4(&sm.k[i16 * S + 16 * rt + 4 * h4]), St[rt], ks);
-      } else {
-#pragma unroll
-        for (int m = 0; m < NT / 2; ++m) {
-          const uint4 ak = exact8(&sm.k[i16 * S + 32 * m + 4 * h4]);
-          uint4 bh, bl;
-          split8m(St[2 * m], St[2 * m + 1], negI, bh, bl);
-          ks = mma32(ak, bl, mma32(ak, bh, ks));
-        }
-      }
-      f32x4 R;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) R[r] = gt.bet[r] * (vc[r] - gt.gam[r] * ks[r]);
-      const f32x4 U = mm(Tt, R, z4());
-      const f32x4 dU = gt.del * U;
-      uint2 uh, ul;
-      if constexpr (!F32IN) split4(dU, uh, ul);
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
-        f32x4 akt;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) akt[s] = sm.k[(4 * h4 + s) * S + 16 * rt + i16];
-        if constexpr (F32IN) {
-          St[rt] = mm(akt, dU, gt.gam_last * St[rt]);
-        } else {
-          const uint2 a = pack4(akt);
-          St[rt] = mma16b(a, ul, mma16b(a, uh, gt.gam_last * St[rt]));
-        }
-      }
+      fwd_chunk_state<D, F32IN>(St, sm.k, sm.g, sm.b, Tt, vc, negI, h4, i16);
       __syncthreads();
     }
   }
@@ -290,8 +310,12 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
   const int t_beg = a.seg_off[seg], t_end = a.seg_off[seg + 1];
   const int nc = (t_end - t_beg + L - 1) / L;
   const size_t DD = size_t(D) * D;
-  const size_t cstride = size_t(a.h_v) * DD;  // between consecutive chunks in the workspace
-  const float* hws = a.hws + (size_t(a.gchunk[seg]) * a.h_v + h) * DD;
+  const size_t cstride = size_t(a.h_v) * DD;  // between consecutive checkpoints in the workspace
+  // The start states of chunks 0, kBwdCkpt, 2 kBwdCkpt, ... of the segment
+  // (states kernel), and this work-group's scratch for the start states of
+  // the chunks after one of them, re-run forward when the walk reaches them.
+  const float* hws = a.hws + (size_t(a.gck[seg]) * a.h_v + h) * DD;
+  float* const scr = a.scr + size_t(blockIdx.x) * (kBwdCkpt - 1) * DD;
   // T, KK and QK of every chunk (from the prep kernel), [16, 16] fp32 each.
   constexpr int TW = 3 * L * L;
   const size_t tstride = size_t(a.h_v) * TW;
@@ -378,12 +402,86 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
       return f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u), __uint_as_float(x.y << 16),
                    __uint_as_float(x.y & 0xffff0000u)};
   };
+  // Forward re-run of chunks c0 .. c1 - 2 from the checkpoint ckp = S0(c0):
+  // S0(c + 1) goes to scratch slot c - c0 (tile layout, as load_ws reads it),
+  // stepped by the same code as the states kernel, so bitwise its values.
+  auto rerun = [&](int c0, int c1, const float* ckp) {
+    f32x4 St[NT];
+    load_ws(ckp, St);
+    // Inputs of chunk c, fetched one chunk ahead as raw words from rows
+    // clamped into the chunk (converted and masked when staged), as in the
+    // states kernel.  Every lane-dependent offset is recomputed from an
+    // opaque copy of the thread id, so that none is held across the chunk
+    // loop below, whose registers are full.
+    KRaw kr;
+    VRaw vr[4];
+    f32x4 Ttn;
+    float gr = 0.f, br = 0.f;
+    auto load = [&](int c) {
+      int tl = tid;
+      asm volatile("" : "+v"(tl));
+      const int ln = tl & 63, lh4 = ln >> 4, li16 = ln & 15, lcol = 16 * (tl >> 6) + li16;
+      const int lrow = tl / (D / 4), lcol4 = 4 * (tl % (D / 4));
+      const int t0 = t_beg + c * L;
+      const int nf = min(L, t_end - t0);
+      kr = *reinterpret_cast<const KRaw*>(static_cast<const VRaw*>(a.k) +
+                                          (size_t(t0 + min(lrow, nf - 1)) * a.h_qk + hq) * D + lcol4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * lh4 + r;
+        vr[r] = static_cast<const VRaw*>(a.v)[(size_t(t0 + min(row, nf - 1)) * a.h_v + h) * D + lcol];
+        Ttn[r] = tws[c * tstride + li16 * L + row];
+      }
+      if (tl < L) {
+        const size_t gi = size_t(t0 + min(tl, nf - 1)) * a.h_v + h;
+        gr = a.g[gi];
+        br = a.beta[gi];
+      }
+    };
+    load(c0);
+    for (int c = c0; c + 1 < c1; ++c) {
+      int tl = tid;
+      asm volatile("" : "+v"(tl));
+      const int ln = tl & 63, lh4 = ln >> 4, li16 = ln & 15, lw = tl >> 6;
+      const int lrow = tl / (D / 4), lcol4 = 4 * (tl % (D / 4));
+      const int nf = min(L, t_end - (t_beg + c * L));
+      f32x4 kv = unpack(kr), vc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (F32IN)
+          vc[r] = vr[r];
+        else
+          vc[r] = __uint_as_float(uint32_t(vr[r]) << 16);
+        if (4 * lh4 + r >= nf) vc[r] = 0.f;
+      }
+      if (lrow >= nf) kv = z4();
+      *reinterpret_cast<f32x4*>(&sm.k[lrow * S + lcol4]) = kv;
+      if (tl < L) {
+        sm.g[tl] = tl < nf ? gr : 0.f;
+        sm.b[tl] = tl < nf ? br : 0.f;
+      }
+      const f32x4 Tt = Ttn;
+      __syncthreads();
+      if (c + 2 < c1) load(c + 1);
+      fwd_chunk_state<D, F32IN>(St, sm.k, sm.g, sm.b, Tt, vc, neg_identity(lh4, li16), lh4, li16);
+      float* const p = scr + size_t(c - c0) * DD;
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) *reinterpret_cast<f32x4*>(p + (rt * NT + lw) * 256 + 4 * ln) = St[rt];
+      __syncthreads();  // K, g and beta of the chunk read
+    }
+  };
+
   fetch(nc - 1);
 
-  for (int c = nc - 1; c >= 0; --c) {
+  for (int blk = (nc - 1) / kBwdCkpt; blk >= 0; --blk) {
+  const int c0 = blk * kBwdCkpt;
+  const int c1 = min(nc, c0 + kBwdCkpt);
+  const float* const ckp = hws + blk * cstride;
+  if (c1 - c0 > 1) rerun(c0, c1, ckp);
+  for (int c = c1 - 1; c >= c0; --c) {
     const int t0 = t_beg + c * L;
     const int n = min(L, t_end - t0);
-    const float* s0p = hws + c * cstride;
+    const float* s0p = c == c0 ? ckp : scr + size_t(c - c0 - 1) * DD;
     f32x4 S0[NT];
     load_ws(s0p, S0);
     f32x4 T, Tt, kk, qk;
@@ -662,6 +760,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
         a.dbeta[size_t(t0 + i) * a.h_v + h] = db + eb;
       }
     }
+  }
   }
 
   // Start-state gradient: to the parent (summed there over its children) or

@@ -93,6 +93,11 @@ hipError_t launch_scan_d128(const ScanArgs& a, bool paths, hipStream_t stream);
 // Whether (d_k, d_v, dtype) has a compiled scan kernel.
 bool scan_supported(int d_k, int d_v, int dtype);
 
+// The scan backward keeps the start state of every kBwdCkpt-th chunk of a
+// segment (a checkpoint) and re-runs the chunks between two checkpoints
+// forward when it reaches them.
+constexpr int kBwdCkpt = 8;
+
 struct ScanBwdArgs {
   const void* q;
   const void* k;
@@ -109,7 +114,10 @@ struct ScanBwdArgs {
   float* dg;             // [N, h_v]
   float* dbeta;          // [N, h_v]
   float* dinit;          // [n_roots, h_v, d, d] or null
-  float* hws;            // workspace: chunk start states [total_chunks, h_v, d, d]
+  float* hws;            // workspace: checkpoint start states, every kBwdCkpt-th chunk of a segment
+                         // (segment s's j-th at slot gck[s] + j) [total_ckpts, h_v, d, d]
+  float* scr;            // workspace: per level work-group, the start states of the chunks after a
+                         // checkpoint, re-run from it [n_items * h_v, kBwdCkpt - 1, d, d]
   float* tws;            // workspace: chunk T, KK, QK [total_chunks, h_v, 3, 16, 16]
   float* dsseg;          // workspace: start-state gradients [n_seg, h_v, d, d]
   const int32_t* seg_off;
@@ -119,6 +127,7 @@ struct ScanBwdArgs {
   const int32_t* kid;
   const int32_t* gchunk;
   const int32_t* chunk_seg;
+  const int32_t* gck;    // first checkpoint slot of each segment
   int32_t n_chunks;      // total chunks (prep launch)
   int32_t n_seg;         // segments (states launch)
   const int32_t* items;  // segments of this level

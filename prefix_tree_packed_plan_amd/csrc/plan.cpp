@@ -235,11 +235,14 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
       if (p.parents[i] >= 0) p.kid[fill[p.parents[i]]++] = i;
   }
   p.gchunk.assign(n_seg, 0);
+  p.gck.assign(n_seg, 0);
   for (int32_t i = 0; i < n_seg; ++i) {
     p.gchunk[i] = static_cast<int32_t>(p.total_chunks);
+    p.gck[i] = static_cast<int32_t>(p.total_ckpts);
     const int32_t nc = (p.lens[i] + Plan::kBwdChunk - 1) / Plan::kBwdChunk;
     for (int32_t j = 0; j < nc; ++j) p.chunk_seg.push_back(i);
     p.total_chunks += nc;
+    p.total_ckpts += (nc + Plan::kBwdCkpt - 1) / Plan::kBwdCkpt;
   }
 
   // Device mirror.
@@ -261,7 +264,8 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   p.m_kid = p.m_kid_off + p.kid_off.size();
   p.m_gchunk = p.m_kid + p.kid.size();
   p.m_chunk_seg = p.m_gchunk + p.gchunk.size();
-  p.mirror.resize(p.m_chunk_seg + p.chunk_seg.size());
+  p.m_gck = p.m_chunk_seg + p.chunk_seg.size();
+  p.mirror.resize(p.m_gck + p.gck.size());
   std::copy(p.seg_off.begin(), p.seg_off.end(), p.mirror.begin() + p.m_seg_off);
   std::copy(p.parents.begin(), p.parents.end(), p.mirror.begin() + p.m_parent);
   std::copy(p.slot.begin(), p.slot.end(), p.mirror.begin() + p.m_slot);
@@ -280,6 +284,7 @@ int build_plan(const int32_t* parents, const int32_t* seg_lens, int32_t n_seg,
   std::copy(p.kid.begin(), p.kid.end(), p.mirror.begin() + p.m_kid);
   std::copy(p.gchunk.begin(), p.gchunk.end(), p.mirror.begin() + p.m_gchunk);
   std::copy(p.chunk_seg.begin(), p.chunk_seg.end(), p.mirror.begin() + p.m_chunk_seg);
+  std::copy(p.gck.begin(), p.gck.end(), p.mirror.begin() + p.m_gck);
 
   *out = std::move(p);
   return TREE_OK;

@@ -60,16 +60,21 @@ struct Plan {
   // gradients are summed into s's final-state gradient).  gchunk[s] is the
   // offset of s's first kBwdChunk-token chunk among all chunks in segment
   // order, chunk_seg[c] the segment of chunk c (total_chunks of them).
+  // The backward keeps the start state of every kBwdCkpt-th chunk of a
+  // segment; gck[s] is the offset of s's first such checkpoint among all of
+  // them in segment order (total_ckpts of them).
   static constexpr int32_t kBwdChunk = 16;
-  std::vector<int32_t> kid_off, kid, gchunk, chunk_seg;
+  static constexpr int32_t kBwdCkpt = 8;
+  std::vector<int32_t> kid_off, kid, gchunk, chunk_seg, gck;
   int64_t total_chunks = 0;
+  int64_t total_ckpts = 0;
 
   // Device copy: one int32 array; element offsets of each table inside it.
   std::vector<int32_t> mirror;
   size_t m_seg_off = 0, m_parent = 0, m_slot = 0, m_hist = 0, m_order = 0, m_root = 0, m_ctx = 0;
   size_t m_path_off = 0, m_path_seg = 0;
   size_t m_ent_off = 0, m_ent = 0, m_fut_off = 0, m_fut = 0, m_roots = 0;
-  size_t m_kid_off = 0, m_kid = 0, m_gchunk = 0, m_chunk_seg = 0;
+  size_t m_kid_off = 0, m_kid = 0, m_gchunk = 0, m_chunk_seg = 0, m_gck = 0;
 
   size_t device_bytes() const { return mirror.size() * sizeof(int32_t); }
 };

@@ -190,14 +190,17 @@ void check_plan(const Trie& t, int32_t W, const char* name) {
     const std::vector<int32_t> got(p.kid.begin() + p.kid_off[s], p.kid.begin() + p.kid_off[s + 1]);
     CHECK(got == kids[s], "%s: kid list of %d", name, s);
   }
-  int64_t chunks = 0;
+  int64_t chunks = 0, ckpts = 0;
   for (int32_t s = 0; s < n; ++s) {
     CHECK(p.gchunk[s] == chunks, "%s: gchunk[%d]", name, s);
+    CHECK(p.gck[s] == ckpts, "%s: gck[%d]", name, s);
     const int32_t nc = (t.lens[s] + tg::Plan::kBwdChunk - 1) / tg::Plan::kBwdChunk;
     for (int32_t j = 0; j < nc; ++j) CHECK(p.chunk_seg[chunks + j] == s, "%s: chunk_seg", name);
     chunks += nc;
+    for (int32_t j = 0; j < nc; j += tg::Plan::kBwdCkpt) ++ckpts;  // chunks 0, 8, 16, ... of the segment
   }
   CHECK(p.total_chunks == chunks && static_cast<int64_t>(p.chunk_seg.size()) == chunks, "%s: total_chunks", name);
+  CHECK(p.total_ckpts == ckpts && static_cast<int64_t>(p.gck.size()) == n, "%s: total_ckpts", name);
   std::vector<int32_t> roots;
   for (int32_t s = 0; s < n; ++s)
     if (t.parents[s] < 0) roots.push_back(s);
@@ -249,7 +252,7 @@ void check_plan(const Trie& t, int32_t W, const char* name) {
             same(p.ent_off, p.m_ent_off) && same(p.ent, p.m_ent) && same(p.fut_off, p.m_fut_off) &&
             same(p.fut, p.m_fut) && same(p.roots, p.m_roots) && same(p.kid_off, p.m_kid_off) &&
             same(p.kid, p.m_kid) && same(p.gchunk, p.m_gchunk) && same(p.chunk_seg, p.m_chunk_seg) &&
-            p.m_chunk_seg + p.chunk_seg.size() == p.mirror.size(),
+            same(p.gck, p.m_gck) && p.m_gck + p.gck.size() == p.mirror.size(),
         "%s: device mirror", name);
 }
 

@@ -301,11 +301,13 @@ def test_schedule_constants_match_the_header():
 
 @pytest.mark.parametrize("cid", sorted(CONFIGS))
 def test_scan_backward_workspace_size_and_checks(cid):
-    """Workspace = the start state and [16, 16] T, KK, QK tiles of every
-    16-token chunk + one start-state gradient per segment (+ per-value-head
-    dq, dk when more than two value heads share a q/k head; two add straight
-    into dq, dk), fp32; undersized workspaces and bad arguments are rejected
-    before any device work."""
+    """Workspace = checkpoint start states (every 8th 16-token chunk of a
+    segment) + one start-state
+    gradient per segment + the [16, 16] T, KK, QK tiles of every chunk + the
+    re-run scratch of the largest level's work-groups (7 states each) (+
+    per-value-head dq, dk when more than two value heads share a q/k head;
+    two add straight into dq, dk), fp32; undersized workspaces and bad
+    arguments are rejected before any device work."""
     lib = _lib.load()
     parents, lens, _ = make_trie(cid)
     s = CONFIGS[cid]
@@ -316,15 +318,23 @@ def test_scan_backward_workspace_size_and_checks(cid):
     chunks = [int(sum((lens[i] + 15) // 16 for i in range(len(parents)) if depth[i] == lv))
               for lv in range(int(depth.max()) + 1)]
     dd = s.d_k * s.d_v
-    want = (sum(chunks) + len(parents)) * s.h_v * dd + sum(chunks) * s.h_v * 3 * 16 * 16  # + every chunk's T, KK, QK
+    levels = np.bincount(depth)
+    total = sum(chunks)
+
+    ckpts = int(sum((int((lens[i] + 15) // 16) + 7) // 8 for i in range(len(parents))))
+
+    def base(h_v):
+        return (ckpts + len(parents)) * h_v * dd + total * h_v * 3 * 16 * 16 + int(levels.max()) * h_v * 7 * dd
+
+    want = base(s.h_v)
     if s.h_v > 2 * s.h_qk:
         want += 2 * int(lens.sum()) * s.h_v * s.d_k
     need = lib.tree_gdn_scan_backward_workspace_bytes(plan.handle, s.h_qk, s.h_v, s.d_k, s.d_v)
     assert need == 4 * want
     # Four value heads per q/k head: the per-value-head parts are needed.
     need4 = lib.tree_gdn_scan_backward_workspace_bytes(plan.handle, 1, 4, s.d_k, s.d_v)
-    base4 = (sum(chunks) + len(parents)) * 4 * dd + sum(chunks) * 4 * 3 * 16 * 16
-    assert need4 == 4 * (base4 + 2 * int(lens.sum()) * 4 * s.d_k)
+    assert need4 == 4 * (base(4) + 2 * int(lens.sum()) * 4 * s.d_k)
+
     fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     bwd = lib.tree_gdn_scan_backward
     n = plan.n_tokens
