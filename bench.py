@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -209,7 +210,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=5,
                     help="workload: 1 tiny, 2 GRPO group, 3 chains, 4 agentic trie, 5 RL batch trie (default)")
     ap.add_argument("--schedule", choices=["auto", "level", "rescan"], default="auto",
@@ -298,8 +299,10 @@ def main():
         step(events[k], k)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    conv_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    scan_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    conv_t = [e[0].elapsed_time(e[1]) for e in events]
+    scan_t = [e[1].elapsed_time(e[2]) for e in events]
+    conv_ms = sum(conv_t) / args.steps
+    scan_ms = sum(scan_t) / args.steps
     if flush is None:
         ms_per_step = 1e3 * wall / args.steps
         timing = "wall clock over the timed steps (synchronised on both sides)"
@@ -416,10 +419,10 @@ def main():
 
     n_levels = st["n_levels"] if sched == "level" else 1
     kernels = {
-        "tree_conv": {"ms": conv_ms, "bytes": conv_b, "launches": 1,
-                      "GB/s": conv_b / conv_ms / 1e6},
-        "tree_gdn_scan": {"ms": scan_ms, "bytes": scan_b, "launches": n_levels,
-                          "GB/s": scan_b / scan_ms / 1e6},
+        "tree_conv": {"ms": conv_ms, "ms_median": statistics.median(conv_t), "ms_min": min(conv_t),
+                      "bytes": conv_b, "launches": 1, "GB/s": conv_b / conv_ms / 1e6},
+        "tree_gdn_scan": {"ms": scan_ms, "ms_median": statistics.median(scan_t), "ms_min": min(scan_t),
+                          "bytes": scan_b, "launches": n_levels, "GB/s": scan_b / scan_ms / 1e6},
     }
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     kd = kernels[dom]
@@ -469,6 +472,10 @@ def main():
             "parallelism": "1 GPU",
         },
         "timing": timing,
+        # per-step HIP event times (conv + scan) over the timed steps
+        "event_ms_per_step": {"mean": conv_ms + scan_ms,
+                              "median": statistics.median([a + b for a, b in zip(conv_t, scan_t)]),
+                              "min": min(a + b for a, b in zip(conv_t, scan_t))},
         "roofline": roofline,
         "kernels": kernels,
         "roofline_combined_frac": ((conv_b + scan_b) / (HBM_PEAK_GBS * 1e9)) / ((conv_ms + scan_ms) * 1e-3),
