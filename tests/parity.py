@@ -11,6 +11,7 @@ The bar (fp64 oracle on the same bf16/fp32 inputs):
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -26,6 +27,15 @@ STATE_RTOL = 1e-4
 # 1e-6 of the fp64 result at these sizes; 1e-4 keeps two orders of margin and
 # fails an output path that drops the lo parts (~2e-3 on the tiny trie).
 OUT_ATOL_F32 = 1e-4
+
+
+# Every output and state comparison of the session, for the run's summary
+# (tests/conftest.py prints the worst of each kind after the tests).
+RECORDS: list = []
+
+
+def _record(kind, **vals):
+    RECORDS.append(dict(kind=kind, test=os.environ.get("PYTEST_CURRENT_TEST", "").split(" (")[0], **vals))
 
 
 def out_atol(dtype) -> float:
@@ -70,10 +80,11 @@ def out_errs(gpu_t, ref, rows=None, cols=None):
             "asserted": float((d - rounding_allowance(ref, gpu_t.dtype)).max())}
 
 
-def out_err(gpu_t, ref, rows=None, cols=None, log=True):
+def out_err(gpu_t, ref, rows=None, cols=None, log=True, what="output"):
     """The asserted output error (see out_errs); the raw and beyond-rounding
     figures are printed to stderr."""
     e = out_errs(gpu_t, ref, rows, cols)
+    _record(what, dtype=str(gpu_t.dtype).replace("torch.", ""), **e)
     if log:
         print(f"    output error: raw max abs {e['raw']:.3e}, beyond bf16 rounding {e['beyond_rounding']:.3e}, "
               f"asserted {e['asserted']:.3e}", file=sys.stderr, flush=True)
@@ -113,7 +124,9 @@ def scan_errors_full(parents, lens, q, k, v, g, beta, o_gpu, st_gpu, scale=1.0, 
                                            init_states=init)
     hs = np.arange(tv.shape[1]) if heads is None else np.asarray(heads)
     sg = to_np(st_gpu)[:, hs]
-    return out_err(o_gpu, o_ref[:, hs], cols=hs), float(state_rel_err(sg, s_ref[:, hs]).max())
+    es = float(state_rel_err(sg, s_ref[:, hs]).max())
+    _record("state", rel=es)
+    return out_err(o_gpu, o_ref[:, hs], cols=hs, what="scan output"), es
 
 
 def _gdn_path_task(a):
@@ -126,7 +139,6 @@ def _gdn_path_task(a):
 def oracle_workers():
     """Worker processes for the pooled oracle: the CPUs this process may use,
     at most 16."""
-    import os
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
@@ -184,11 +196,13 @@ def scan_errors_sampled(parents, lens, q, k, v, g, beta, o_gpu, st_gpu, segments
     raw = 0.0
     for (path, idx, ends, hs), (op, snaps) in zip(meta, results):
         e = out_errs(o_gpu.index_select(0, idx), op, cols=hs)
+        _record("scan output", dtype=str(o_gpu.dtype).replace("torch.", ""), **e)
         worst_o = max(worst_o, e["asserted"])
         raw = max(raw, e["raw"])
         for p, en in zip(path, ends):
             sg = to_np(st_gpu[p])[hs]
             worst_s = max(worst_s, float(state_rel_err(sg, snaps[int(en)]).max()))
+    _record("state", rel=worst_s)
     print(f"    sampled scan check: {len(segments)} segments x {sum(len(b) for b in blocks)} value heads, "
           f"output raw max abs {raw:.3e}, asserted {worst_o:.3e}, state rel {worst_s:.3e}",
           file=sys.stderr, flush=True)
@@ -206,13 +220,13 @@ def conv_errors(parents, lens, x, w, y_gpu, bias=None, act=None, segments=None, 
     if segments is None:
         ctx = None if init_ctx is None else to_np(init_ctx)[:, :, cs]
         ref = oconv.tree_conv_reference(parents, lens, to_np(x)[:, cs], tw, tb, act, init_ctx=ctx)
-        return out_err(y_gpu, ref, cols=cs)
+        return out_err(y_gpu, ref, cols=cs, what="conv output")
     worst = 0.0
     for s in segments:
         path = otrie.root_path(parents, s)
         idx = torch.as_tensor(otrie.path_token_index(path, lens), device=x.device)
         yp = oconv.conv_on_path(to_np(x.index_select(0, idx))[:, cs], tw, tb, act)
-        worst = max(worst, out_err(y_gpu.index_select(0, idx), yp, cols=cs))
+        worst = max(worst, out_err(y_gpu.index_select(0, idx), yp, cols=cs, what="conv output"))
     return worst
 
 

@@ -52,7 +52,7 @@ def test_conv_backward_matches_the_oracle(dtype, W, C, act):
     f = parity.to_np
     rx, rw, rb, rc = ograd.tree_conv_vjp(parents, lens, f(t["x"]), f(t["w"]), f(dy), bias=f(t["bias"]), act=act,
                                          init_ctx=f(init))
-    ex = parity.out_err(dx, rx) if dtype == "bf16" else float(np.abs(f(dx) - rx).max())
+    ex = parity.out_err(dx, rx, what="conv backward dx") if dtype == "bf16" else float(np.abs(f(dx) - rx).max())
     say(f"  dx {ex:.3e}  dw {rel(f(dw), rw):.3e}  dbias {rel(f(db), rb):.3e}")
     assert ex <= (parity.OUT_ATOL if dtype == "bf16" else 1e-4)
     assert rel(f(dw), rw) <= 1e-5 and rel(f(db), rb) <= 1e-5

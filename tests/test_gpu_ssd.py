@@ -52,7 +52,7 @@ def test_ssd_matches_the_oracle(dtype, shape):
     hh = host(t)
     ry, rs = ossd.tree_ssd_reference(parents, lens, hh["x"], hh["dt"], hh["A"], hh["B"], hh["C"], hh["D"],
                                      init_states=parity.to_np(init))
-    ey = parity.out_err(y, ry) if dtype == "bf16" else float(np.abs(parity.to_np(y) - ry).max())
+    ey = parity.out_err(y, ry, what="ssd output") if dtype == "bf16" else float(np.abs(parity.to_np(y) - ry).max())
     es = float(parity.state_rel_err(parity.to_np(st), rs).max())
     say(f"  y {ey:.3e}  state {es:.3e}")
     assert ey <= (parity.OUT_ATOL if dtype == "bf16" else Y_F32_ATOL)
@@ -100,7 +100,7 @@ def test_ssd_rl_batch_sampled_segments_and_determinism():
     off = np.concatenate([[0], np.cumsum(wl.seg_lens)])
     for sg in segs:
         rows = np.arange(off[sg], off[sg + 1])
-        ey = parity.out_err(y1[torch.as_tensor(rows, device=DEV)][:, heads], ry[rows][:, heads])
+        ey = parity.out_err(y1[torch.as_tensor(rows, device=DEV)][:, heads], ry[rows][:, heads], what="ssd output")
         es = float(parity.state_rel_err(parity.to_np(st[sg][heads]), rs[sg][heads]).max())
         say(f"  segment {sg}: y {ey:.3e}  state {es:.3e}")
         assert ey <= parity.OUT_ATOL and es <= parity.STATE_RTOL
