@@ -1,0 +1,134 @@
+"""GPU parity on the scan's degenerate cases and extreme trie shapes, against
+the oracle (through the C ABI).
+
+Gates at their limits: no decay with full writes (g = 0, beta = 1: the
+state accumulates over whole paths, the hardest case for its precision), no
+writes (beta = 0), complete forgetting at every token (g = -40), and a random
+mix of these.  Trie shapes: a deep chain run one launch per level, and one
+wide level of single-token segments.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from tests import parity
+from workloads import make_scan_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+RAGGED = [1, 2, 3, 5, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 200, 300]
+
+
+def _lib():
+    import prefix_tree_packed_plan_amd as ptp
+    return ptp
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rand_trie(seed, n_seg, lens_choices, n_roots=1):
+    rng = np.random.default_rng(seed)
+    parents = [-1] * n_roots + [int(rng.integers(0, i)) for i in range(n_roots, n_seg)]
+    lens = rng.choice(lens_choices, size=n_seg)
+    return np.array(parents, np.int32), np.array(lens, np.int32)
+
+
+def _gates(case, n, h_v, seed):
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    if case == "no_decay":
+        g, b = torch.zeros(n, h_v), torch.ones(n, h_v)
+    elif case == "no_write":
+        g = -torch.nn.functional.softplus(torch.randn(n, h_v, generator=gen))
+        b = torch.zeros(n, h_v)
+    elif case == "full_forget":
+        g, b = torch.full((n, h_v), -40.0), torch.sigmoid(torch.randn(n, h_v, generator=gen))
+    else:  # mix
+        g = torch.where(torch.rand(n, h_v, generator=gen) < 0.5, 0.0, -40.0)
+        b = (torch.rand(n, h_v, generator=gen) < 0.5).float()
+    return g.to(DEV).contiguous(), b.to(DEV).contiguous()
+
+
+@pytest.mark.parametrize("case", ["no_decay", "no_write", "full_forget", "mix"])
+@pytest.mark.parametrize("dtype,d,h_qk,h_v", [("f32", 32, 1, 2), ("bf16", 64, 1, 2), ("bf16", 128, 2, 4)])
+def test_scan_degenerate_gates(case, dtype, d, h_qk, h_v):
+    """Both schedules agree bit for bit, from zero and from given root
+    states, and match the oracle.  Without writes and from zero states the
+    outputs and states are exactly zero."""
+    ptp = _lib()
+    parents, lens = rand_trie(31, 20, RAGGED, n_roots=2)
+    n = int(lens.sum())
+    say(f"degenerate gates {case} dtype={dtype} d={d} heads={h_qk}/{h_v} N={n}")
+    t = make_scan_inputs(n, h_qk, h_v, d, d, dtype, DEV, seed=21)
+    t["g"], t["beta"] = _gates(case, n, h_v, 22)
+    plan = ptp.tree_plan(parents, lens, 4)
+    gen = torch.Generator(device="cpu").manual_seed(23)
+    init = (torch.randn(2, h_v, d, d, generator=gen) * 0.1).to(DEV)
+    for init_states in (None, init):
+        kw = {} if init_states is None else {"init_states": init_states}
+        o1, s1 = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, scale=0.75,
+                                   return_states=True, schedule="level", **kw)
+        o2, s2 = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, scale=0.75,
+                                   return_states=True, schedule="rescan", **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
+        assert torch.isfinite(o1.float()).all() and torch.isfinite(s1).all()
+        if case == "no_write" and init_states is None:
+            assert not o1.float().abs().max().item() and not s1.abs().max().item()
+        eo, es = parity.scan_errors_full(parents, lens, t["q"], t["k"], t["v"], t["g"], t["beta"], o1, s1,
+                                         scale=0.75, init_states=init_states)
+        say(f"  init={'given' if init_states is not None else 'zero'}: out {eo:.3e}  state {es:.3e}")
+        assert eo <= parity.out_atol(dtype) and es <= parity.STATE_RTOL
+
+
+def test_deep_chain_one_launch_per_level():
+    """A chain of 400 segments of 1-5 tokens forced onto the level schedule
+    (400 launches, each segment starting from its parent's state in a
+    workspace slot or in `states`) equals the rescan and the oracle."""
+    ptp = _lib()
+    rng = np.random.default_rng(41)
+    lens = rng.integers(1, 6, size=400).astype(np.int32)
+    parents = np.arange(-1, len(lens) - 1, dtype=np.int32)
+    n = int(lens.sum())
+    say(f"deep chain: 400 levels, N={n}")
+    t = make_scan_inputs(n, 2, 4, 128, 128, "bf16", DEV, seed=42)
+    plan = ptp.tree_plan(parents, lens, 4)
+    o1, s1 = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, return_states=True,
+                               schedule="level")
+    o2 = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, schedule="level")
+    o3, s3 = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, return_states=True,
+                               schedule="rescan")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3) and torch.equal(s1, s3)
+    eo, es = parity.scan_errors_full(parents, lens, t["q"], t["k"], t["v"], t["g"], t["beta"], o1, s1)
+    say(f"  out {eo:.3e}  state {es:.3e}")
+    assert eo <= parity.OUT_ATOL and es <= parity.STATE_RTOL
+
+
+def test_wide_level_of_single_token_segments():
+    """One 100-token root with 3000 children of 1-3 tokens: a level of 3000
+    segments x 4 value heads, each a partial chunk starting from the root's
+    state.  Both schedules agree bit for bit; sampled leaves match the
+    oracle."""
+    ptp = _lib()
+    rng = np.random.default_rng(43)
+    lens = np.concatenate([[100], rng.integers(1, 4, size=3000)]).astype(np.int32)
+    parents = np.array([-1] + [0] * 3000, np.int32)
+    n = int(lens.sum())
+    say(f"wide level: 3000 children, N={n}")
+    t = make_scan_inputs(n, 2, 4, 128, 128, "bf16", DEV, seed=44)
+    plan = ptp.tree_plan(parents, lens, 4)
+    o1, s1 = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, return_states=True,
+                               schedule="level")
+    o2, s2 = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, return_states=True,
+                               schedule="rescan")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    segs = [1, 2, 1500, 2999, 3000]
+    eo, es = parity.scan_errors_sampled(parents, lens, t["q"], t["k"], t["v"], t["g"], t["beta"], o1, s1, segs)
+    say(f"  out {eo:.3e}  state {es:.3e}")
+    assert eo <= parity.OUT_ATOL and es <= parity.STATE_RTOL
