@@ -132,3 +132,47 @@ def test_wide_level_of_single_token_segments():
     eo, es = parity.scan_errors_sampled(parents, lens, t["q"], t["k"], t["v"], t["g"], t["beta"], o1, s1, segs)
     say(f"  out {eo:.3e}  state {es:.3e}")
     assert eo <= parity.OUT_ATOL and es <= parity.STATE_RTOL
+
+
+@pytest.mark.parametrize("case", ["no_decay", "full_forget", "mix"])
+@pytest.mark.parametrize("dtype,d,h_qk,h_v", [("f32", 32, 1, 2), ("bf16", 128, 2, 4)])
+def test_scan_backward_degenerate_gates(case, dtype, d, h_qk, h_v):
+    """The scan backward under the degenerate gates, from given root states
+    and final-state gradients: every gradient against autograd of the fp64
+    token-by-token oracle, within the backward's 2e-5 bar (max-norm
+    relative).  The gate gradient is measured against the larger of its own
+    and the beta gradient's max-norm: both are sums over a token's row of the
+    same products, and under complete forgetting the true dg vanishes (about
+    1e-17 here) while the fp32 chunk sums of its terms, of dbeta's size, leave
+    rounding of that size (about 6e-8)."""
+    from oracle import grad as ograd
+    ptp = _lib()
+    parents, lens = rand_trie(51, 12, [1, 3, 16, 17, 33, 40], n_roots=2)
+    n = int(lens.sum())
+    say(f"scan backward, degenerate gates {case} dtype={dtype} d={d} heads={h_qk}/{h_v} N={n}")
+    t = make_scan_inputs(n, h_qk, h_v, d, d, dtype, DEV, seed=52)
+    t["g"], t["beta"] = _gates(case, n, h_v, 53)
+    do = make_scan_inputs(n, h_qk, h_v, d, d, dtype, DEV, seed=54)["v"]
+    gen = torch.Generator(device="cpu").manual_seed(55)
+    init = (torch.randn(2, h_v, d, d, generator=gen) * 0.3).to(DEV)
+    dst = (torch.randn(len(parents), h_v, d, d, generator=gen) * 0.1).to(DEV)
+    plan = ptp.tree_plan(parents, lens, 4)
+    _, states = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, scale=0.6,
+                                  return_states=True, init_states=init, schedule="level")
+    got = ptp.tree_gdn_scan_backward(t["q"], t["k"], t["v"], t["g"], t["beta"], do, plan, states, scale=0.6,
+                                     init_states=init, dstates=dst)
+    torch.cuda.synchronize()
+    f = parity.to_np
+    ref = ograd.tree_gdn_vjp(parents, lens, f(t["q"]), f(t["k"]), f(t["v"]), f(t["g"]), f(t["beta"]), f(do),
+                             scale=0.6, init_states=f(init), dstates=f(dst))
+    names = ("dq", "dk", "dv", "dg", "dbeta", "dinit")
+    errs = {}
+    for nm, a, b in zip(names, got, ref):
+        scale = np.abs(b).max()
+        if nm == "dg":
+            scale = max(scale, np.abs(ref[4]).max())
+        errs[nm] = float(np.abs(f(a) - b).max() / max(scale, 1e-30))
+    say("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    say(f"  max |dg| {np.abs(f(got[3])).max():.3e} (oracle {np.abs(ref[3]).max():.3e}), "
+        f"max |dbeta| {np.abs(ref[4]).max():.3e}")
+    assert max(errs.values()) <= 2e-5, errs
