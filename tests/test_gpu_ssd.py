@@ -104,3 +104,42 @@ def test_ssd_rl_batch_sampled_segments_and_determinism():
         es = float(parity.state_rel_err(parity.to_np(st[sg][heads]), rs[sg][heads]).max())
         say(f"  segment {sg}: y {ey:.3e}  state {es:.3e}")
         assert ey <= parity.OUT_ATOL and es <= parity.STATE_RTOL
+
+
+@pytest.mark.parametrize("case", ["no_decay", "full_forget", "large_step"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ssd_degenerate_decay(case, dtype):
+    """The decay at its limits, given root states, D on; outputs and every
+    final state against the oracle.  no_decay: A dt -> 0, the state sums every
+    token of the path.  full_forget: A dt = -80 at every token with a small
+    step (A = -8000, dt = 0.01), so the state holds only the last token's
+    write.  large_step: the same decay through dt = 5 (A = -16), which also
+    scales the writes and puts outputs in the hundreds; the fp32 path carries
+    its products as split bf16 (2^-16 of the sum of the terms' magnitudes), so
+    there its bar is 1e-4 of the largest output rather than 1e-4 absolute."""
+    from oracle import ssd as ossd
+    ptp = __import__("prefix_tree_packed_plan_amd")
+    G, H, N, P = 2, 4, 128, 64
+    parents, lens = rand_trie(83, 18, [1, 3, 16, 17, 33, 40, 64], n_roots=2)
+    n = int(lens.sum())
+    say(f"ssd degenerate decay {case} dtype={dtype} N={n}")
+    t = make_ssd_inputs(n, G, H, N, P, dtype, DEV, seed=6)
+    A, dt = {"no_decay": (-1e-6, 0.05), "full_forget": (-8000.0, 0.01), "large_step": (-16.0, 5.0)}[case]
+    t["A"] = torch.full_like(t["A"], A)
+    t["dt"] = torch.full_like(t["dt"], dt)
+    g = torch.Generator().manual_seed(7)
+    init = (torch.randn((2, H, N, P), generator=g) * 0.3).to(DEV)
+    plan = ptp.tree_plan(parents, lens, 4)
+    y, st = ptp.tree_ssd_scan(t["x"], t["dt"], t["A"], t["B"], t["C"], plan, D=t["D"], return_states=True,
+                              init_states=init)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all() and torch.isfinite(st).all()
+    hh = host(t)
+    ry, rs = ossd.tree_ssd_reference(parents, lens, hh["x"], hh["dt"], hh["A"], hh["B"], hh["C"], hh["D"],
+                                     init_states=parity.to_np(init))
+    ey = parity.out_err(y, ry, what="ssd output") if dtype == "bf16" else float(np.abs(parity.to_np(y) - ry).max())
+    es = float(parity.state_rel_err(parity.to_np(st), rs).max())
+    say(f"  y {ey:.3e} (max |y| {np.abs(ry).max():.3e})  state {es:.3e}")
+    f32_bar = Y_F32_ATOL * (np.abs(ry).max() if case == "large_step" else 1.0)
+    assert ey <= (parity.OUT_ATOL if dtype == "bf16" else f32_bar)
+    assert es <= parity.STATE_RTOL
