@@ -33,7 +33,10 @@
 //                            O^T += U^T P^T;  S = gamma_L S + K^T W.
 //
 // Products that feed the state carry their fp32 operand as hi + lo bf16
-// (relative 2^-17; lo x lo dropped); the output path uses hi only.  The
+// (relative 2^-17; lo x lo dropped); the output path uses hi only.  Where the
+// decay inside a chunk makes the second row block's share of K S0 or Q S0
+// (scaled by gamma_i) no larger than the error the other rows already carry,
+// those MFMAs are not issued (part 1 has one instantiation per such class).  The
 // state's own split takes its exact residual S - hi from an MFMA (split4m),
 // which leaves the vector ALU two conversions per pair of values.  The
 // output is produced transposed, so a lane holds 4 consecutive value columns
@@ -204,6 +207,8 @@ struct Smem {
   alignas(16) float abb[2][256];
   // Gate tables of the chunk in buffer s: G log2(e), exp(G), beta, exp(G_L - G).
   alignas(16) float gt[2][4][CH];
+  // Largest gamma of the chunk's second 16-row block (rows 16..31).
+  alignas(16) float gmax1[2];
   alignas(16) float graw[2][CH];
   alignas(16) float braw[2][CH];
   // Output rows of the previous chunk, 256 bytes per token, 16-byte chunk c
@@ -376,13 +381,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     x += lane >= 16 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15)) : 0.f;
     const float g2 = x * kLog2e;
     const float g2L = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), CH - 1));
+    const float gam = ex2(g2);
     if (lane < CH) {
       float* gt = &sm.gt[buf][0][0];
       gt[lane] = g2;
-      gt[CH + lane] = ex2(g2);
+      gt[CH + lane] = gam;
       gt[2 * CH + lane] = lane < L ? sm.braw[buf][lane] : 0.f;
       gt[3 * CH + lane] = ex2(g2L - g2);
     }
+    // Max of gamma over rows 16..31 (lane row 1): a running max along the row.
+    float gm = lane >= 16 && lane < CH ? gam : 0.f;
+    gm = fmaxf(gm, dpp_shr(gm, 1));
+    gm = fmaxf(gm, dpp_shr(gm, 2));
+    gm = fmaxf(gm, dpp_shr(gm, 4));
+    gm = fmaxf(gm, dpp_shr(gm, 8));
+    gm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gm), CH - 1));
+    if (lane == 0) sm.gmax1[buf] = gm;
   };
 
   // Whole token rows of the staged output, by the DMA waves (rows 16(cw -
@@ -525,23 +539,49 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     // -- state, part 1: R = diag(b)(V - gamma K S0), O^T = scale gamma (S0^T Q^T)
     // S is decayed by gamma_L for the update of part 2 as soon as each pair
     // of tiles has been split, far ahead of the MFMAs that accumulate into it.
+    //
+    // Rows 16..31 enter both products scaled by their gamma_i <= g1 (the
+    // block's largest).  With S0 = hi + lo (|S0 - hi| <= 2^-9 |S0|, the lo
+    // pass leaving 2^-18), a term is dropped only where its bound falls to
+    // what the other rows already carry: the lo pass of K S0 when g1 <= 2^-10
+    // (g1 2^-9 < 2^-18 of sum |K||S0|), Q S0 when g1 <= 2^-12 (below the
+    // 2^-9 of the hi-only output product of rows 0..15), and the hi pass of
+    // K S0 too when g1 <= 2^-18.  The class is uniform over the work-group.
     const float gL = gtw[CH + CH - 1];
     f32x4 R[2], OT[2];
     R[0] = R[1] = OT[0] = OT[1] = zero4();
+    auto part1 = [&](auto cls) {
+      constexpr int C = decltype(cls)::value;  // 0: all terms, 1: no lo pass, 2: no Q S0, 3: no K S0 (rows 16..31)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint4 sh, sl;
-      split8m(S[2 * kk], S[2 * kk + 1], negI, sh, sl);
-      S[2 * kk] *= gL;
-      S[2 * kk + 1] *= gL;
+      for (int kk = 0; kk < 4; ++kk) {
+        uint4 sh, sl;
+        split8m(S[2 * kk], S[2 * kk + 1], negI, sh, sl);
+        S[2 * kk] *= gL;
+        S[2 * kk + 1] *= gL;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const uint4 ak = ld_a8(Ks + ROW16 * b, ao[kk], ao2[kk]);
-        const uint4 aq = ld_a8(Qs + ROW16 * b, ao[kk], ao2[kk]);
-        R[b] = mma32(ak, sh, R[b]);
-        R[b] = mma32(ak, sl, R[b]);
-        OT[b] = mma32(sh, aq, OT[b]);
+        for (int b = 0; b < 2; ++b) {
+          if (b == 0 || C < 3) {
+            const uint4 ak = ld_a8(Ks + ROW16 * b, ao[kk], ao2[kk]);
+            R[b] = mma32(ak, sh, R[b]);
+            if (b == 0 || C < 1) R[b] = mma32(ak, sl, R[b]);
+          }
+          if (b == 0 || C < 2) {
+            const uint4 aq = ld_a8(Qs + ROW16 * b, ao[kk], ao2[kk]);
+            OT[b] = mma32(sh, aq, OT[b]);
+          }
+        }
       }
+    };
+    {
+      const float g1 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.gmax1[s])));
+      if (g1 > 0x1p-10f)
+        part1(std::integral_constant<int, 0>{});
+      else if (g1 > 0x1p-12f)
+        part1(std::integral_constant<int, 1>{});
+      else if (g1 > 0x1p-18f)
+        part1(std::integral_constant<int, 2>{});
+      else
+        part1(std::integral_constant<int, 3>{});
     }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
