@@ -571,6 +571,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
           }
         }
       }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(&gtw[2 * CH + 16 * b + 4 * h4]);
+        const f32x4 vv = bf4(ld_tr(Vs + ROW16 * b, vo));
+        // R = b (v - gamma K S0), the subtraction fused (one rounding) in every
+        // instantiation; without K S0 (rows 16..31 of class 3) R = b v.
+        if (b == 0 || C < 3) {
+          const f32x4 gv = *reinterpret_cast<const f32x4*>(&gtw[CH + 16 * b + 4 * h4]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) R[b][r] = bv[r] * __builtin_fmaf(-gv[r], R[b][r], vv[r]);
+        } else {
+          R[b] = bv * vv;
+        }
+        if (b == 0 || C < 2) OT[b] *= args.scale * gtw[CH + 16 * b + i16];
+      }
     };
     {
       const float g1 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sm.gmax1[s])));
@@ -582,14 +597,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         part1(std::integral_constant<int, 2>{});
       else
         part1(std::integral_constant<int, 3>{});
-    }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const f32x4 gv = *reinterpret_cast<const f32x4*>(&gtw[CH + 16 * b + 4 * h4]);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(&gtw[2 * CH + 16 * b + 4 * h4]);
-      const f32x4 vv = bf4(ld_tr(Vs + ROW16 * b, vo));
-      R[b] = bv * (vv - gv * R[b]);
-      OT[b] *= args.scale * gtw[CH + 16 * b + i16];
     }
     __syncthreads();  // (D) the inverse, -A and P^T operands of every wave are in LDS
 
