@@ -566,6 +566,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
             if (b == 0 || C < 1) R[b] = mma32(ak, sl, R[b]);
           }
           if (b == 0 || C < 2) {
+            // Kept apart from the K read at the same offsets: fused into one
+            // ds_read2st64_b64 they cost several times as much.
+            asm volatile("" ::: "memory");
             const uint4 aq = ld_a8(Qs + ROW16 * b, ao[kk], ao2[kk]);
             OT[b] = mma32(sh, aq, OT[b]);
           }
