@@ -353,6 +353,9 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
 #pragma unroll
     for (int m = 0; m < NT / 2; ++m) {
       const uint4 ac = tile_a8(Cs, ao[m], ao2[m]);
+      // Kept apart from the C read at the same offsets: fused into one
+      // ds_read2st64_b64 they cost several times as much.
+      asm volatile("" ::: "memory");
       const uint4 ab = tile_a8(Bs, ao[m], ao2[m]);
       qkt = mma32(ab, ac, qkt);
       uint4 sh, sl;
