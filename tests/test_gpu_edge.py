@@ -176,3 +176,44 @@ def test_scan_backward_degenerate_gates(case, dtype, d, h_qk, h_v):
     say(f"  max |dg| {np.abs(f(got[3])).max():.3e} (oracle {np.abs(ref[3]).max():.3e}), "
         f"max |dbeta| {np.abs(ref[4]).max():.3e}")
     assert max(errs.values()) <= 2e-5, errs
+
+
+@pytest.mark.parametrize("h_qk,h_v", [(2, 4)])
+def test_scan_decay_classes(h_qk, h_v):
+    """The d = 128 kernel drops terms of a chunk's rows 16..31 by the largest
+    gamma of those rows (lo pass of K S0 at <= 2^-10, Q S0 at <= 2^-12, all
+    of K S0 at <= 2^-18).  Gates built so that chunks land on each side of
+    every threshold: g = 0 except at row 16 of a chunk, where it sets
+    G_16 = ln(target); so gamma is 1 on rows 0..15 and the target on rows
+    16..31.  Both schedules agree bit for bit and match the oracle."""
+    ptp = _lib()
+    targets = [2.0 ** e for e in (-9, -10.5, -11, -12.5, -15, -18.5, -20, -30)]
+    rng = np.random.default_rng(61)
+    lens = np.array([32 * 6, 32 * 5 + 17, 32 * 4, 20, 32 * 3 + 31], np.int32)
+    parents = np.array([-1, 0, 0, 1, 2], np.int32)
+    n = int(lens.sum())
+    say(f"decay classes N={n}")
+    t = make_scan_inputs(n, h_qk, h_v, 128, 128, "bf16", DEV, seed=62)
+    g = torch.zeros(n, h_v)
+    off = np.concatenate([[0], np.cumsum(lens)])
+    k = 0
+    for s in range(len(lens)):
+        for c0 in range(int(off[s]), int(off[s + 1]), 32):
+            if c0 + 16 < off[s + 1]:
+                for hh in range(h_v):
+                    g[c0 + 16, hh] = float(np.log(targets[(k + hh) % len(targets)]))
+                k += 1
+    t["g"] = g.to(DEV).contiguous()
+    plan = ptp.tree_plan(parents, lens, 4)
+    gen = torch.Generator(device="cpu").manual_seed(63)
+    init = (torch.randn(1, h_v, 128, 128, generator=gen) * 0.3).to(DEV)
+    o1, s1 = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, return_states=True,
+                               init_states=init, schedule="level")
+    o2, s2 = ptp.tree_gdn_scan(t["q"], t["k"], t["v"], t["g"], t["beta"], plan, return_states=True,
+                               init_states=init, schedule="rescan")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    eo, es = parity.scan_errors_full(parents, lens, t["q"], t["k"], t["v"], t["g"], t["beta"], o1, s1,
+                                     init_states=init)
+    say(f"  out {eo:.3e}  state {es:.3e}")
+    assert eo <= parity.OUT_ATOL and es <= parity.STATE_RTOL
