@@ -312,7 +312,10 @@ size_t tree_workspace_bytes(const tree_plan_t* plan, int32_t h_v, int32_t d_k, i
  * scale  multiplies q (1.0 = the plain recurrence).
  * dtype  TREE_DTYPE_BF16 (bf16 MFMA, fp32 accumulation, compensated
  *        split-bf16 on the state path) or TREE_DTYPE_F32 (inputs split into
- *        two bf16 parts on every product).
+ *        two bf16 parts on every product).  At d = 128 in bf16, a chunk's
+ *        later rows skip the products their decay scales below the error
+ *        the other rows already carry; the results depend on the inputs only
+ *        (both schedules give the same bits).
  * sched  TREE_SCHED_LEVEL, TREE_SCHED_RESCAN or TREE_SCHED_AUTO (see
  *        tree_plan_choose_schedule).
  * dplan, dplan_bytes  as for tree_conv.
