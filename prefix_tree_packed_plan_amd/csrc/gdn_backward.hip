@@ -76,7 +76,7 @@ struct BwdSmem {
   alignas(16) float b[L];
   alignas(16) float gl[NW][4];          // per-wave partial sum(S0 o dS1)
   alignas(16) float rows[NW][3][L];     // per-wave partial row sums
-  alignas(16) float m[2][L * 17];       // M and dA o KK o Gamma
+  alignas(16) float m[3][L * 17];       // M, M^T and dA o KK o Gamma
   // Per-wave 16x16 partials (dR U^T, dOs U^T): part in the lanes'
   // accumulator order (lane l's 4 values at 4l), part_t the transpose in the
   // same order, so that either orientation is one 16-byte read per lane.
@@ -298,7 +298,9 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  // Wave-uniform; as a scalar at d = 128 (scalar LDS offsets leave room in
+  // the vector registers there).
+  const int w = D == 128 && !F32IN ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int h4 = lane >> 4;
   const int i16 = lane & 15;
   const int col = 16 * w + i16;
@@ -648,8 +650,10 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * h4 + r;
-        sm.m[0][row * 17 + i16] = (dP[r] * qk[r] + dA[r] * gt.bet[r] * kk[r]) * gt.Gm[r];
-        sm.m[1][row * 17 + i16] = dA[r] * kk[r] * gt.Gm[r];
+        const float mv = (dP[r] * qk[r] + dA[r] * gt.bet[r] * kk[r]) * gt.Gm[r];
+        sm.m[0][row * 17 + i16] = mv;
+        sm.m[1][i16 * 17 + row] = mv;
+        sm.m[2][row * 17 + i16] = dA[r] * kk[r] * gt.Gm[r];
       }
     }
     f32x4 kc, qc;
@@ -728,36 +732,40 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     if (c > 0) fetch(c - 1);
     __syncthreads();  // every read of this chunk's tables done
 
-    if (w == 0 && lane < L) {  // gate gradients of token i = lane
-      const int i = lane;
-      float d_gam = 0.f, d_dl = 0.f, db = 0.f, gl = 0.f, rs = 0.f, cs = 0.f, eb = 0.f;
+    if (w == 0 && lane < 3 * L) {  // gate gradients of token i = lane % 16
+      // Lanes 16 p + i (p = 0, 1, 2) each gather one of the three per-token
+      // partial sums over the waves and one row sum of a 16 x 16 table:
+      // (d_gam, row i of M), (d_dl, row i of M^T), (db, row i of
+      // dA o KK o Gamma).  Every sum keeps the order of a single lane's loop.
+      const int i = lane & 15, p = lane >> 4;
+      float s1 = 0.f, s2 = 0.f, gl = 0.f;
 #pragma unroll
       for (int v = 0; v < NT; ++v) {
-        d_gam += sm.rows[v][0][i];
-        d_dl += sm.rows[v][1][i];
-        db += sm.rows[v][2][i];
+        s1 += sm.rows[v][p][i];
         gl += sm.gl[v][0] + sm.gl[v][1] + sm.gl[v][2] + sm.gl[v][3];
       }
+      const float* const mp = &sm.m[p][i * 17];
 #pragma unroll
-      for (int j = 0; j < L; ++j) {
-        rs += sm.m[0][i * 17 + j];
-        cs += sm.m[0][j * 17 + i];
-        eb += sm.m[1][i * 17 + j];
-      }
-      const float dl = gt.del_c * d_dl;
-      const float dl_sum = row_sum16(dl);
-      float dG = gt.gam_c * d_gam - dl + rs - cs;
-      if (i == L - 1) dG += gt.gam_last * gl + dl_sum;
-      // dg_t = sum of dG_i over i >= t within the chunk.
-      float dg = 0.f;
+      for (int j = 0; j < L; ++j) s2 += mp[j];
+      const float d_dl = __shfl(s1, i + L, 64), db = __shfl(s1, i + 2 * L, 64);
+      const float cs = __shfl(s2, i + L, 64), eb = __shfl(s2, i + 2 * L, 64);
+      if (lane < L) {
+        const float d_gam = s1, rs = s2;
+        const float dl = gt.del_c * d_dl;
+        const float dl_sum = row_sum16(dl);
+        float dG = gt.gam_c * d_gam - dl + rs - cs;
+        if (i == L - 1) dG += gt.gam_last * gl + dl_sum;
+        // dg_t = sum of dG_i over i >= t within the chunk.
+        float dg = 0.f;
 #pragma unroll
-      for (int j = 0; j < L; ++j) {
-        const float x = __shfl(dG, j, 64);
-        dg += j >= i ? x : 0.f;
-      }
-      if (i < n) {
-        a.dg[size_t(t0 + i) * a.h_v + h] = dg;
-        a.dbeta[size_t(t0 + i) * a.h_v + h] = db + eb;
+        for (int j = 0; j < L; ++j) {
+          const float x = __shfl(dG, j, 64);
+          dg += j >= i ? x : 0.f;
+        }
+        if (i < n) {
+          a.dg[size_t(t0 + i) * a.h_v + h] = dg;
+          a.dbeta[size_t(t0 + i) * a.h_v + h] = db + eb;
+        }
       }
     }
   }
