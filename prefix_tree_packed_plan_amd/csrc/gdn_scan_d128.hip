@@ -259,20 +259,26 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
                       (j == 2 ? 0xBF80u : 0u) | (j == 3 ? 0xBF800000u : 0u));
   }
 
-  // Block -> (item, value head).  When value heads come in pairs per q/k head
-  // and h_v is a multiple of 16, the pair lands on blocks b and b + 8, which
-  // the dispatcher places on the same XCD, so the second read of their q and
-  // k tiles is served by that XCD's L2.
+  // Block -> (item, value head), XCD-aware.  The dispatcher deals blocks to
+  // the 8 XCDs in turn (block b on XCD b % 8).  Within each run of 4 items,
+  // XCDs 2i and 2i + 1 take the two halves of item i's value heads, so each
+  // token's g and beta (one 128-byte line holds all heads' values) are
+  // fetched into two L2s rather than all eight, and value heads that share a
+  // q/k head (adjacent heads) read its tiles through one L2.  Items past the
+  // last whole run, and head counts not a multiple of 4, keep the plain
+  // order.  (One XCD per item fetched 8% less but was not faster.)
   int item, h;
   {
     const int b = blockIdx.x;
-    item = b / args.h_v;
-    const int r = b - item * args.h_v;
-    if (args.h_v == 2 * args.h_qk && args.h_v % 16 == 0) {
-      const int p = r & 15;
-      h = 2 * ((r >> 4) * 8 + (p & 7)) + (p >> 3);
+    const int full = (args.n_items / 4) * 4;
+    if (args.h_v % 4 == 0 && b < full * args.h_v) {
+      const int gi = b / (4 * args.h_v), r = b - gi * 4 * args.h_v;
+      const int x = r & 7;
+      item = 4 * gi + (x >> 1);
+      h = (x & 1) * (args.h_v >> 1) + (r >> 3);
     } else {
-      h = r;
+      item = b / args.h_v;
+      h = b - item * args.h_v;
     }
   }
   const int hq = h / (args.h_v / args.h_qk);
