@@ -842,10 +842,20 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(ScanBwdArgs a) {
   // Two value heads per q/k head add into dq and dk in the level launches:
   // the first of the pair clears the chunk's rows here, before them.
   if (a.dq_accum && (h & 1) == 0) {
-    for (int e = lane; e < n * D; e += 64) {
-      const size_t o = (size_t(t0 + e / D) * a.dq_heads + hq) * D + (e % D);
-      a.dq[o] = 0.f;
-      a.dk[o] = 0.f;
+    if (((reinterpret_cast<uintptr_t>(a.dq) | reinterpret_cast<uintptr_t>(a.dk)) & 15) == 0) {
+      // Whole rows in 16-byte pieces, non-temporal: the rows are next touched
+      // by the level launches, long after.
+      for (int e = lane; e < n * (D / 4); e += 64) {
+        const size_t o = (size_t(t0 + e / (D / 4)) * a.dq_heads + hq) * D + 4 * (e % (D / 4));
+        __builtin_nontemporal_store(z4(), reinterpret_cast<f32x4*>(a.dq + o));
+        __builtin_nontemporal_store(z4(), reinterpret_cast<f32x4*>(a.dk + o));
+      }
+    } else {
+      for (int e = lane; e < n * D; e += 64) {
+        const size_t o = (size_t(t0 + e / D) * a.dq_heads + hq) * D + (e % D);
+        a.dq[o] = 0.f;
+        a.dk[o] = 0.f;
+      }
     }
   }
 }
