@@ -521,8 +521,33 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.h_v = h_v;
   a.scale = scale;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  // Checkpoints: at bf16 d = 128 from the forward scan kernel (32-token
+  // chunks, all segments in one launch from the given final states), else
+  // from the states kernel.
+  const bool ck_fwd = d_k == 128 && d_v == 128 && dtype == TREE_DTYPE_BF16;
   {
-    const hipError_t e = tg::launch_scan_backward_prep(a, d_k, dtype, st);
+    hipError_t e = tg::launch_scan_backward_prep(a, d_k, dtype, !ck_fwd, st);
+    if (e == hipSuccess && ck_fwd) {
+      tg::ScanArgs c{};
+      c.q = q;
+      c.k = k;
+      c.v = v;
+      c.g = g;
+      c.beta = beta;
+      c.init = init_states;
+      c.root_idx = a.root_idx;
+      c.states = const_cast<float*>(states);  // read only in this pass
+      c.seg_off = a.seg_off;
+      c.parent = a.parent;
+      c.items = base + p.m_order;  // every segment, level by level
+      c.n_items = p.n_seg;
+      c.h_qk = h_qk;
+      c.h_v = h_v;
+      c.scale = scale;
+      c.ckpt = a.hws;
+      c.gck = a.gck;
+      e = tg::launch_scan_d128_checkpoints(c, st);
+    }
     if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);
   }
   // Deepest level first: a parent sums its children's start-state gradients.

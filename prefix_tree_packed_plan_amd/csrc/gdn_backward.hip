@@ -35,10 +35,13 @@
 // (I + N)(I + N^2)(I + N^4)(I + N^8), N = -A: six 16x16 MFMA products.
 //
 // Launches: a prep kernel computes every chunk's T, KK and QK (state-free, all
-// chunks at once); a states kernel re-runs every segment forward from its
+// chunks at once); a checkpoint pass re-runs every segment forward from its
 // parent's final state (the forward's `states`; all segments at once) and
-// writes every chunk's start state to the workspace; then one launch per
-// trie level, deepest first, walks each segment's chunks backwards.  Work
+// writes the start state of every kBwdCkpt-th chunk to the workspace (the
+// states kernel below, or at bf16 d = 128 the forward scan kernel's own
+// checkpoint instantiation); then one launch per trie level, deepest first,
+// walks each segment's chunks backwards, re-running the chunks between two
+// checkpoints forward when it reaches them.  Work
 // item: one segment and one value head per work-group of d/16 waves; wave w
 // owns column tile w (16 columns) of every [16, d] chunk tensor and of the
 // state gradient dS, which stays in MFMA accumulator registers across the
@@ -119,8 +122,10 @@ __device__ __forceinline__ void solve(const f32x4 kk, const Gates& s, int h4, in
 // K rows (row stride D + 4), g and beta, staged in LDS; Tt: the lane's tile of
 // T^T; vc: the lane's V values (rows 4 h4 + 0..3 of its column), zero past
 // the segment end.  The states kernel and the level kernel's re-run of the
-// chunks after a checkpoint both step the state here, so the re-run start
-// states are bitwise the states kernel's.
+// chunks after a checkpoint both step the state here, so where the states
+// kernel takes the checkpoints the re-run start states are bitwise its own.
+// (At bf16 d = 128 the checkpoints come from the forward scan kernel, whose
+// 32-token chunks round differently; the re-run starts from them.)
 template <int D, bool F32IN>
 __device__ __forceinline__ void fwd_chunk_state(f32x4 (&St)[D / 16], const float* sk, const float* sg, const float* sb,
                                                 const f32x4 Tt, const f32x4 vc, const uint2 negI, int h4, int i16) {
@@ -882,12 +887,12 @@ hipError_t launch_bwd_level(const ScanBwdArgs& a, hipStream_t stream) {
 }
 
 template <int D, bool F32IN>
-hipError_t launch_prep(const ScanBwdArgs& a, hipStream_t stream) {
+hipError_t launch_prep(const ScanBwdArgs& a, bool states, hipStream_t stream) {
   const int64_t items = int64_t(a.n_chunks) * a.h_v;
   if (items <= 0) return hipSuccess;
   gdn_bwd_prep_kernel<D, F32IN><<<dim3(unsigned((items + 3) / 4)), dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !states) return e;
   gdn_bwd_states_kernel<D, F32IN><<<dim3(unsigned(a.n_seg * a.h_v)), dim3(4 * D), 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -898,12 +903,12 @@ bool scan_backward_supported(int d_k, int d_v, int dtype) {
   return d_k == d_v && (d_k == 32 || d_k == 64 || d_k == 128) && (dtype == TREE_DTYPE_BF16 || dtype == TREE_DTYPE_F32);
 }
 
-hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream) {
+hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, bool states, hipStream_t stream) {
   const bool f32 = dtype == TREE_DTYPE_F32;
   switch (d) {
-    case 32: return f32 ? launch_prep<32, true>(a, stream) : launch_prep<32, false>(a, stream);
-    case 64: return f32 ? launch_prep<64, true>(a, stream) : launch_prep<64, false>(a, stream);
-    case 128: return f32 ? launch_prep<128, true>(a, stream) : launch_prep<128, false>(a, stream);
+    case 32: return f32 ? launch_prep<32, true>(a, states, stream) : launch_prep<32, false>(a, states, stream);
+    case 64: return f32 ? launch_prep<64, true>(a, states, stream) : launch_prep<64, false>(a, states, stream);
+    case 128: return f32 ? launch_prep<128, true>(a, states, stream) : launch_prep<128, false>(a, states, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -242,8 +242,16 @@ __device__ __forceinline__ f32x4 gram(const char* X, const char* Y, const int* a
 // of a root-to-leaf path in order with the state carried in registers from
 // one to the next; outputs and states are written only for the segments the
 // walk owns.
-template <bool PATHS>
+// CK: the checkpoint pass of the scan backward instead of the forward: every
+// segment at once from its parent's final state (the forward's `states`,
+// read only), storing the start state of every 4th chunk (every 128 tokens)
+// at the backward's checkpoint slots, with no output, no Q and no state
+// publication.
+static_assert(kBwdCkpt * 16 == 4 * CH, "a checkpoint every 128 tokens: every 8th 16-token backward chunk");
+
+template <bool PATHS, bool CK = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4))) void gdn_d128_kernel(ScanArgs args) {
+  static_assert(!(PATHS && CK), "checkpoints are taken per segment");
   __shared__ Smem sm;
 
   const int tid = threadIdx.x;
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         const int ok = row * rs_qk + cofs, ov = row * rs_v + cofs;
         const int lo = blk_off(blk);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sm.kb[buf] + lo), 16, ok, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sm.qb[buf] + lo), 16, ok, 0, 0, 0);
+        if constexpr (!CK) __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sm.qb[buf] + lo), 16, ok, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sm.vb[buf] + lo), 16, ov, 0, 0, 0);
       }
     }
@@ -450,7 +458,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     // The previous chunk's output rows leave right after the next chunk's
     // DMA is issued (not ahead of it), a whole chunk before the wait above
     // has to count them.
-    if (prev_t0 >= 0 && prev_own) store_out(prev_t0, prev_L);
+    if constexpr (!CK) {
+      if (prev_t0 >= 0 && prev_own) store_out(prev_t0, prev_L);
+    } else if ((((t0 - seg_beg) / CH) & 3) == 0) {
+      // Checkpoint (t0 - seg_beg) / 128 of the segment: S is this chunk's
+      // start state; tile (mt, cw) in the lanes' accumulator order.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      float* const dst =
+          args.ckpt + (static_cast<size_t>(args.gck[seg] + (t0 - seg_beg) / (4 * CH)) * args.h_v + h) * head_elems +
+          cw * 256 + 4 * ln;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) __builtin_nontemporal_store(S[mt], reinterpret_cast<f32x4*>(dst + mt * 8 * 256));
+    }
 
     // -- gate tables of this chunk (made by wave GW during the previous one)
     const float* gtw = &sm.gt[s][0][0];
@@ -527,7 +547,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       uint2 vh, vl;
       split4(v, vh, vl);
       sm.ttab[2][lane] = make_uint4(vh.x, vh.y, vl.x, vl.y);
-    } else if (cw == 3 || cw >= 6) {
+    } else if (!CK && (cw == 3 || cw >= 6)) {
       // P^T block (jb, ib) = (0, 0), (0, 1), (1, 1): lane i (query), rows j (key).
       const int jb = cw == 7 ? 1 : 0, ib = cw == 3 ? 0 : 1;
       const f32x4 d = gram(Ks + ROW16 * jb, Qs + ROW16 * ib, ao, ao2);
@@ -571,7 +591,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
             R[b] = mma32(ak, sh, R[b]);
             if (b == 0 || C < 1) R[b] = mma32(ak, sl, R[b]);
           }
-          if (b == 0 || C < 2) {
+          if (!CK && (b == 0 || C < 2)) {
             // Kept apart from the K read at the same offsets: fused into one
             // ds_read2st64_b64 they cost several times as much.
             asm volatile("" ::: "memory");
@@ -593,7 +613,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         } else {
           R[b] = bv * vv;
         }
-        if (b == 0 || C < 2) OT[b] *= args.scale * gtw[CH + 16 * b + i16];
+        if (!CK && (b == 0 || C < 2)) OT[b] *= args.scale * gtw[CH + 16 * b + i16];
       }
     };
     {
@@ -622,8 +642,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       split4(U1, u1h, u1l);
 
       const uint4 uh = make_uint4(u0h.x, u0h.y, u1h.x, u1h.y);
-      OT[0] = mma32(uh, sm.ptab[0][lane], OT[0]);
-      OT[1] = mma32(uh, sm.ptab[1][lane], OT[1]);
+      if constexpr (!CK) {
+        OT[0] = mma32(uh, sm.ptab[0][lane], OT[0]);
+        OT[1] = mma32(uh, sm.ptab[1][lane], OT[1]);
+      }
 
       uint4 wh, wl;
       {
@@ -640,14 +662,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         S[mt] = mma32(a, wl, S[mt]);
       }
       // Stage this chunk's output: token 16b + i16, value columns col_w + 4h4..+3.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int li = ln & 15, lh = ln >> 4;
-      const int sto_w = li * 256 + 16 * ((2 * cw + (lh >> 1)) ^ li) + 8 * (lh & 1);
+      if constexpr (!CK) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int li = ln & 15, lh = ln >> 4;
+        const int sto_w = li * 256 + 16 * ((2 * cw + (lh >> 1)) ^ li) + 8 * (lh & 1);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        *reinterpret_cast<uint2*>(sm.ost + sto_w + b * 16 * 256) =
-            make_uint2(pk2(OT[b][0], OT[b][1]), pk2(OT[b][2], OT[b][3]));
+        for (int b = 0; b < 2; ++b)
+          *reinterpret_cast<uint2*>(sm.ost + sto_w + b * 16 * 256) =
+              make_uint2(pk2(OT[b][0], OT[b][1]), pk2(OT[b][2], OT[b][3]));
+      }
     }
     prev_t0 = t0;
     prev_L = Lc;
@@ -676,10 +700,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     s ^= 1;
   }
   __syncthreads();  // every wave's staged rows of the last chunk
-  if (prev_own) store_out(prev_t0, prev_L);
+  if constexpr (!CK) {
+    if (prev_own) store_out(prev_t0, prev_L);
+  }
 
   // ---- segment end: publish the state -------------------------------------------
-  if (!PATHS) {
+  if (!PATHS && !CK) {
     float* dst = nullptr;
     if (args.states)
       dst = args.states + (static_cast<size_t>(seg) * args.h_v + h) * head_elems;
@@ -695,6 +721,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 }
 
 }  // namespace
+
+hipError_t launch_scan_d128_checkpoints(const ScanArgs& a, hipStream_t stream) {
+  if (a.n_items <= 0) return hipSuccess;
+  gdn_d128_kernel<false, true><<<dim3(static_cast<unsigned>(a.n_items) * a.h_v), 64 * NW, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_scan_d128(const ScanArgs& a, bool paths, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.n_items) * a.h_v);
