@@ -521,12 +521,13 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.h_v = h_v;
   a.scale = scale;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  // Checkpoints: at bf16 d = 128 from the forward scan kernel (32-token
-  // chunks, all segments in one launch from the given final states), else
-  // from the states kernel.
+  // Checkpoints and the chunk tables: at bf16 d = 128 from the forward scan
+  // kernel (32-token chunks, all segments in one launch from the given final
+  // states; prep then only clears dq, dk), else from the prep and states
+  // kernels.
   const bool ck_fwd = d_k == 128 && d_v == 128 && dtype == TREE_DTYPE_BF16;
   {
-    hipError_t e = tg::launch_scan_backward_prep(a, d_k, dtype, !ck_fwd, st);
+    hipError_t e = tg::launch_scan_backward_prep(a, d_k, dtype, !ck_fwd, !ck_fwd, st);
     if (e == hipSuccess && ck_fwd) {
       tg::ScanArgs c{};
       c.q = q;
@@ -546,6 +547,8 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
       c.scale = scale;
       c.ckpt = a.hws;
       c.gck = a.gck;
+      c.tws = a.tws;
+      c.gchunk = a.gchunk;
       e = tg::launch_scan_d128_checkpoints(c, st);
     }
     if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);

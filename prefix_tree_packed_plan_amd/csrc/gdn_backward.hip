@@ -790,7 +790,9 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 // all chunks of the trie run in parallel before the level launches.  One
 // wave per (chunk, value head); tokens past a segment's end are zero rows
 // with g = beta = 0, as in the level kernel.
-template <int D, bool F32IN>
+// TABLES = false: only the clearing of dq, dk below (the tables come from the
+// forward kernel's checkpoint pass).
+template <int D, bool F32IN, bool TABLES>
 __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(ScanBwdArgs a) {
   __shared__ float sg[4][L], sb[4][L];
   const int lane = threadIdx.x & 63;
@@ -805,45 +807,49 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(ScanBwdArgs a) {
   const int hq = h / (a.h_v / a.h_qk);
   const int t0 = a.seg_off[seg] + (c - a.gchunk[seg]) * L;
   const int n = live ? min(L, a.seg_off[seg + 1] - t0) : 0;
-  if (lane < L) {
-    const bool tin = lane < n;
-    sg[w][lane] = tin ? a.g[size_t(t0 + lane) * a.h_v + h] : 0.f;
-    sb[w][lane] = tin ? a.beta[size_t(t0 + lane) * a.h_v + h] : 0.f;
-  }
-  const bool rin = i16 < n;
-  const size_t rbase = (size_t(t0 + (rin ? i16 : 0)) * a.h_qk + hq) * D;
-  f32x4 kk = z4(), qk = z4();
-  if constexpr (F32IN) {
-#pragma unroll
-    for (int m = 0; m < D / 16; ++m) {
-      const f32x4 ak = rin ? load4<true>(a.k, rbase + 16 * m + 4 * h4) : z4();
-      const f32x4 aq = rin ? load4<true>(a.q, rbase + 16 * m + 4 * h4) : z4();
-      kk = mm(ak, ak, kk);
-      qk = mm(aq, ak, qk);
+  if constexpr (TABLES) {
+    if (lane < L) {
+      const bool tin = lane < n;
+      sg[w][lane] = tin ? a.g[size_t(t0 + lane) * a.h_v + h] : 0.f;
+      sb[w][lane] = tin ? a.beta[size_t(t0 + lane) * a.h_v + h] : 0.f;
     }
-  } else {
+    const bool rin = i16 < n;
+    const size_t rbase = (size_t(t0 + (rin ? i16 : 0)) * a.h_qk + hq) * D;
+    f32x4 kk = z4(), qk = z4();
+    if constexpr (F32IN) {
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) {
-      const size_t i0 = rbase + 32 * m + 4 * h4;
-      const uint4 ak = rin ? cat(pack4(load4<false>(a.k, i0)), pack4(load4<false>(a.k, i0 + 16))) : make_uint4(0, 0, 0, 0);
-      const uint4 aq = rin ? cat(pack4(load4<false>(a.q, i0)), pack4(load4<false>(a.q, i0 + 16))) : make_uint4(0, 0, 0, 0);
-      kk = mma32(ak, ak, kk);  // bf16 x bf16 products are exact in fp32
-      qk = mma32(aq, ak, qk);
+      for (int m = 0; m < D / 16; ++m) {
+        const f32x4 ak = rin ? load4<true>(a.k, rbase + 16 * m + 4 * h4) : z4();
+        const f32x4 aq = rin ? load4<true>(a.q, rbase + 16 * m + 4 * h4) : z4();
+        kk = mm(ak, ak, kk);
+        qk = mm(aq, ak, qk);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        const size_t i0 = rbase + 32 * m + 4 * h4;
+        const uint4 ak = rin ? cat(pack4(load4<false>(a.k, i0)), pack4(load4<false>(a.k, i0 + 16))) : make_uint4(0, 0, 0, 0);
+        const uint4 aq = rin ? cat(pack4(load4<false>(a.q, i0)), pack4(load4<false>(a.q, i0 + 16))) : make_uint4(0, 0, 0, 0);
+        kk = mma32(ak, ak, kk);  // bf16 x bf16 products are exact in fp32
+        qk = mma32(aq, ak, qk);
+      }
+    }
+    __syncthreads();
+    const Gates gt = make_gates(sg[w], sb[w], h4, i16);
+    f32x4 T, Tt;
+    solve(kk, gt, h4, i16, T, Tt);
+    if (live) {
+      float* tp = a.tws + (size_t(c) * a.h_v + h) * (3 * L * L);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = (4 * h4 + r) * L + i16;
+        tp[e] = T[r];
+        tp[L * L + e] = kk[r];
+        tp[2 * L * L + e] = qk[r];
+      }
     }
   }
-  __syncthreads();
-  const Gates gt = make_gates(sg[w], sb[w], h4, i16);
-  f32x4 T, Tt;
-  solve(kk, gt, h4, i16, T, Tt);
   if (!live) return;
-  float* tp = a.tws + (size_t(c) * a.h_v + h) * (3 * L * L);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int e = (4 * h4 + r) * L + i16;
-    tp[e] = T[r];
-    tp[L * L + e] = kk[r];
-    tp[2 * L * L + e] = qk[r];
-  }
   // Two value heads per q/k head add into dq and dk in the level launches:
   // the first of the pair clears the chunk's rows here, before them.
   if (a.dq_accum && (h & 1) == 0) {
@@ -887,10 +893,13 @@ hipError_t launch_bwd_level(const ScanBwdArgs& a, hipStream_t stream) {
 }
 
 template <int D, bool F32IN>
-hipError_t launch_prep(const ScanBwdArgs& a, bool states, hipStream_t stream) {
+hipError_t launch_prep(const ScanBwdArgs& a, bool tables, bool states, hipStream_t stream) {
   const int64_t items = int64_t(a.n_chunks) * a.h_v;
   if (items <= 0) return hipSuccess;
-  gdn_bwd_prep_kernel<D, F32IN><<<dim3(unsigned((items + 3) / 4)), dim3(256), 0, stream>>>(a);
+  if (tables)
+    gdn_bwd_prep_kernel<D, F32IN, true><<<dim3(unsigned((items + 3) / 4)), dim3(256), 0, stream>>>(a);
+  else
+    gdn_bwd_prep_kernel<D, F32IN, false><<<dim3(unsigned((items + 3) / 4)), dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !states) return e;
   gdn_bwd_states_kernel<D, F32IN><<<dim3(unsigned(a.n_seg * a.h_v)), dim3(4 * D), 0, stream>>>(a);
@@ -903,12 +912,17 @@ bool scan_backward_supported(int d_k, int d_v, int dtype) {
   return d_k == d_v && (d_k == 32 || d_k == 64 || d_k == 128) && (dtype == TREE_DTYPE_BF16 || dtype == TREE_DTYPE_F32);
 }
 
-hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, bool states, hipStream_t stream) {
+hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, bool tables, bool states,
+                                     hipStream_t stream) {
   const bool f32 = dtype == TREE_DTYPE_F32;
   switch (d) {
-    case 32: return f32 ? launch_prep<32, true>(a, states, stream) : launch_prep<32, false>(a, states, stream);
-    case 64: return f32 ? launch_prep<64, true>(a, states, stream) : launch_prep<64, false>(a, states, stream);
-    case 128: return f32 ? launch_prep<128, true>(a, states, stream) : launch_prep<128, false>(a, states, stream);
+    case 32:
+      return f32 ? launch_prep<32, true>(a, tables, states, stream) : launch_prep<32, false>(a, tables, states, stream);
+    case 64:
+      return f32 ? launch_prep<64, true>(a, tables, states, stream) : launch_prep<64, false>(a, tables, states, stream);
+    case 128:
+      return f32 ? launch_prep<128, true>(a, tables, states, stream)
+                 : launch_prep<128, false>(a, tables, states, stream);
     default: return hipErrorInvalidValue;
   }
 }

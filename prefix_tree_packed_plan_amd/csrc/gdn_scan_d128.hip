@@ -245,8 +245,9 @@ __device__ __forceinline__ f32x4 gram(const char* X, const char* Y, const int* a
 // CK: the checkpoint pass of the scan backward instead of the forward: every
 // segment at once from its parent's final state (the forward's `states`,
 // read only), storing the start state of every 4th chunk (every 128 tokens)
-// at the backward's checkpoint slots, with no output, no Q and no state
-// publication.
+// at the backward's checkpoint slots, and for each 16-token half of a chunk
+// (one backward chunk) its T = (I + A)^-1, K K^T and Q K^T as fp32 16 x 16
+// tables; no output, no Q S0 and no state publication.
 static_assert(kBwdCkpt * 16 == 4 * CH, "a checkpoint every 128 tokens: every 8th 16-token backward chunk");
 
 template <bool PATHS, bool CK = false>
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         const int ok = row * rs_qk + cofs, ov = row * rs_v + cofs;
         const int lo = blk_off(blk);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sm.kb[buf] + lo), 16, ok, 0, 0, 0);
-        if constexpr (!CK) __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sm.qb[buf] + lo), 16, ok, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sm.qb[buf] + lo), 16, ok, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sm.vb[buf] + lo), 16, ov, 0, 0, 0);
       }
     }
@@ -475,6 +476,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     // -- gate tables of this chunk (made by wave GW during the previous one)
     const float* gtw = &sm.gt[s][0][0];
 
+    // CK: the tables of backward chunk 2 (chunk index) + b, rows past the
+    // segment end zeroed (there the backward's rows are zero); none for a
+    // half past the end.
+    const int nb_ck = CK ? min(16, max(0, Lc - 16 * (cw == 7 ? 1 : (cw < 2 ? cw : 0)))) : 0;
+    auto table_rsrc = [&](int b) {
+      const int c16 = 2 * ((t0 - seg_beg) / CH) + b;
+      return rsrc(args.tws + (static_cast<size_t>(args.gchunk[seg] + c16) * args.h_v + h) * (3 * 256), 3 * 256 * 4);
+    };
+
     // -- prep
     if (cw < 2) {
       // Diagonal block cw: A[i][j] = b_i exp(G_i - G_j) k_i.k_j (j < i) and
@@ -486,6 +496,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       // -A is stored by columns: abb[m][p][3 - q] = -A[4q + p][m], so step m
       // reads the 4 - m/4 rows it updates as one contiguous piece.
       const f32x4 d = gram(Ks + ROW16 * cw, Ks + ROW16 * cw, ao, ao2);  // lane i, rows j
+      if constexpr (CK) {
+        if (nb_ck > 0) {  // K K^T[4h + r][i], row-major
+          const auto rt = table_rsrc(cw);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = 4 * h4 + r < nb_ck && i16 < nb_ck ? d[r] : 0.f;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rt, 4 * (256 + (4 * h4 + r) * 16 + i16), 0, 0);
+          }
+        }
+      }
       {
         const float gi = gtw[16 * cw + i16];
         const float bi = gtw[2 * CH + 16 * cw + i16];
@@ -534,6 +554,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         tt[e] = static_cast<uint16_t>(w);
         tt[e + 4] = static_cast<uint16_t>(pk2(t[q] - lo_f(w), 0.f));
       }
+      if constexpr (CK) {
+        if (nb_ck > 0) {  // T[4q + ph][jc], row-major
+          const auto rt = table_rsrc(cw);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(t[q]), rt, 4 * ((4 * q + ph) * 16 + jc), 0, 0);
+        }
+      }
     } else if (cw == 2) {
       // -A_10 as the A operand of R_1 -= A_10 U_0: lane i (token 16 + i),
       // rows j (tokens 0..15).
@@ -547,6 +575,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       uint2 vh, vl;
       split4(v, vh, vl);
       sm.ttab[2][lane] = make_uint4(vh.x, vh.y, vl.x, vl.y);
+    } else if (CK && (cw == 3 || cw == 7)) {
+      // Q K^T of half b = 0 (wave 3) or 1 (wave 7): lane i (key), rows j
+      // (query), stored at [query][key].
+      const int b = cw == 7 ? 1 : 0;
+      const f32x4 d = gram(Qs + ROW16 * b, Ks + ROW16 * b, ao, ao2);
+      if (nb_ck > 0) {
+        const auto rt = table_rsrc(b);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = 4 * h4 + r < nb_ck && i16 < nb_ck ? d[r] : 0.f;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rt, 4 * (512 + (4 * h4 + r) * 16 + i16), 0, 0);
+        }
+      }
     } else if (!CK && (cw == 3 || cw >= 6)) {
       // P^T block (jb, ib) = (0, 0), (0, 1), (1, 1): lane i (query), rows j (key).
       const int jb = cw == 7 ? 1 : 0, ib = cw == 3 ? 0 : 1;

@@ -82,6 +82,8 @@ struct ScanArgs {
   float scale;
   float* ckpt;              // checkpoint pass: the scan backward's checkpoint slots
   const int32_t* gck;       // checkpoint pass: first slot of each segment
+  float* tws;               // checkpoint pass: T, KK, QK of every 16-token chunk [total_chunks, h_v, 3, 16, 16]
+  const int32_t* gchunk;    // checkpoint pass: first 16-token chunk of each segment
 };
 
 // One launch over `n_items` work items x h_v value heads: segments of one
@@ -95,7 +97,8 @@ hipError_t launch_scan_d128(const ScanArgs& a, bool paths, hipStream_t stream);
 // `items` from its parent's final state in `states` (read only; `init` for
 // roots), writing the start state of every kBwdCkpt-th 16-token chunk (every
 // 128 tokens) to ckpt at slot gck[seg] + j, as 16x16 tiles in the lanes'
-// accumulator order; no output.
+// accumulator order, and every 16-token chunk's T, KK and QK to tws (the
+// prep kernel's tables); no output.
 hipError_t launch_scan_d128_checkpoints(const ScanArgs& a, hipStream_t stream);
 
 // Whether (d_k, d_v, dtype) has a compiled scan kernel.
@@ -150,9 +153,11 @@ struct ScanBwdArgs {
 // Scan backward (gdn_backward.hip); d = d_k = d_v.  The prep launches compute
 // every chunk's T, KK and QK (state-free) and every chunk's start state;
 // then one launch per trie level.
-// Prep (T, KK, QK of every chunk; dq, dk cleared where parts are added) and,
-// with `states`, the checkpoint pass of the states kernel.
-hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, bool states, hipStream_t stream);
+// Prep (T, KK, QK of every chunk, unless `tables` is false; dq, dk cleared
+// where parts are added) and, with `states`, the checkpoint pass of the
+// states kernel.
+hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, bool tables, bool states,
+                                     hipStream_t stream);
 hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream);
 // dst[t, j] = sum_m src[t, j group + m] over [n_tok, h_qk * group, d] fp32.
 hipError_t launch_head_group_sum(const float* src, float* dst, int64_t n_tok, int h_qk, int group, int d,
