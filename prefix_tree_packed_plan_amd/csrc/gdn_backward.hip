@@ -35,13 +35,14 @@
 // (I + N)(I + N^2)(I + N^4)(I + N^8), N = -A: six 16x16 MFMA products.
 //
 // Launches: a prep kernel computes every chunk's T, KK and QK (state-free, all
-// chunks at once); a checkpoint pass re-runs every segment forward from its
-// parent's final state (the forward's `states`; all segments at once) and
-// writes the start state of every kBwdCkpt-th chunk to the workspace (the
-// states kernel below, or at bf16 d = 128 the forward scan kernel's own
-// checkpoint instantiation); then one launch per trie level, deepest first,
-// walks each segment's chunks backwards, re-running the chunks between two
-// checkpoints forward when it reaches them.  Work
+// chunks at once) and clears dq, dk where parts are added; a checkpoint pass
+// re-runs every segment forward from its parent's final state (the forward's
+// `states`; all segments at once) and writes the start state of every
+// kBwdCkpt-th chunk to the workspace (the states kernel below; at bf16 d =
+// 128 the forward scan kernel's own checkpoint instantiation, which also
+// writes the chunk tables, so that prep only clears); then one launch per
+// trie level, deepest first, walks each segment's chunks backwards,
+// re-running the chunks between two checkpoints forward when it reaches them.  Work
 // item: one segment and one value head per work-group of d/16 waves; wave w
 // owns column tile w (16 columns) of every [16, d] chunk tensor and of the
 // state gradient dS, which stays in MFMA accumulator registers across the
