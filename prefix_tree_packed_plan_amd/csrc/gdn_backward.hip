@@ -546,13 +546,18 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
         kd = mm(ak, dS[rt], kd);
       }
     } else {
+      // -I for the MFMA split residual, from an opaque lane copy so that it
+      // is not held across the chunk.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const uint2 negI = neg_identity(ln >> 4, ln & 15);
 #pragma unroll
       for (int m = 0; m < NT / 2; ++m) {
         const uint4 ak = exact8(&sm.k[i16 * S + 32 * m + 4 * h4]);
         const uint4 aq = exact8(&sm.q[i16 * S + 32 * m + 4 * h4]);
         uint4 sh, sl, dh, dl;
-        split8(S0[2 * m], S0[2 * m + 1], sh, sl);
-        split8(dS[2 * m], dS[2 * m + 1], dh, dl);
+        split8m(S0[2 * m], S0[2 * m + 1], negI, sh, sl);
+        split8m(dS[2 * m], dS[2 * m + 1], negI, dh, dl);
         ks = mma32(ak, sl, mma32(ak, sh, ks));
         qs = mma32(aq, sl, mma32(aq, sh, qs));
         kd = mma32(ak, dl, mma32(ak, dh, kd));
@@ -679,12 +684,15 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
         xu = mm(gt.del_c * ld4(&sm.u[o4]), ld4(dsr + 16 * jt), xu);
       }
     } else {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const uint2 negI = neg_identity(ln >> 4, ln & 15);
 #pragma unroll
       for (int m = 0; m < NT / 2; ++m) {
         const int o4 = i16 * S + 32 * m + 4 * h4;
         uint4 sh, sl, dh, dl, vh, vl, uh, ul;
-        split8(S0row[2 * m], S0row[2 * m + 1], sh, sl);
-        split8(ld4(dsr + 32 * m), ld4(dsr + 32 * m + 16), dh, dl);
+        split8m(S0row[2 * m], S0row[2 * m + 1], negI, sh, sl);
+        split8m(ld4(dsr + 32 * m), ld4(dsr + 32 * m + 16), negI, dh, dl);
         split8(gt.bet_c * ld4(&sm.r[o4]), gt.bet_c * ld4(&sm.r[o4 + 16]), vh, vl);
         split8(gt.del_c * ld4(&sm.u[o4]), gt.del_c * ld4(&sm.u[o4 + 16]), uh, ul);
         const uint4 ao = exact8(&sm.o[o4]);
