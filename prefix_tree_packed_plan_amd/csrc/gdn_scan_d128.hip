@@ -37,9 +37,9 @@
 // decay inside a chunk makes the second row block's share of K S0 or Q S0
 // (scaled by gamma_i) no larger than the error the other rows already carry,
 // those MFMAs are not issued (part 1 has one instantiation per such class).  The
-// state's own split, and those of R and U in the solve, take their exact
-// residual x - hi from an MFMA (split4m), which leaves the vector ALU two
-// conversions per pair of values.  The
+// state's own split, and those of R in the solve, take their exact residual
+// x - hi from an MFMA (split4m), which leaves the vector ALU two conversions
+// per pair of values.  The
 // output is produced transposed, so a lane holds 4 consecutive value columns
 // of one token.
 //
@@ -677,11 +677,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
       const uint4 t0 = sm.ttab[0][lane], t1 = sm.ttab[1][lane], na = sm.ttab[2][lane];
       split4m(R[0], negI, rh, rl);
       const f32x4 U0 = mma16x3(make_uint2(t0.x, t0.y), make_uint2(t0.z, t0.w), rh, rl, zero4());
-      split4m(U0, negI, u0h, u0l);
+      split4(U0, u0h, u0l);
       R[1] = mma16x3(make_uint2(na.x, na.y), make_uint2(na.z, na.w), u0h, u0l, R[1]);
       split4m(R[1], negI, rh, rl);
       const f32x4 U1 = mma16x3(make_uint2(t1.x, t1.y), make_uint2(t1.z, t1.w), rh, rl, zero4());
-      split4m(U1, negI, u1h, u1l);
+      split4(U1, u1h, u1l);
 
       const uint4 uh = make_uint4(u0h.x, u0h.y, u1h.x, u1h.y);
       if constexpr (!CK) {
