@@ -397,7 +397,7 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     {  // P U on split-bf16 MFMA (hi x hi + hi x lo + lo x hi)
       uint2 ph, pl, uh2, ul2;
       split4m(Pt, negI, ph, pl);
-      split4(U, uh2, ul2);
+      split4m(U, negI, uh2, ul2);
       Y = mma16b(pl, uh2, mma16b(ph, ul2, mma16b(ph, uh2, gt.gam * cs))) + Dh * xv;
     }
     {
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     }
     // -- S = gamma_last S + B^T diag(delta) U
     uint2 uh, ul;
-    split4(gt.del * U, uh, ul);
+    split4m(gt.del * U, negI, uh, ul);
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       St[rt] = mma16b(bT[rt], ul, mma16b(bT[rt], uh, gt.gam_last * St[rt]));
