@@ -351,7 +351,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
   // Chunk at token tc into buffer buf: waves DW0 and DW0 + 1, which have the
   // least work before the chunk barrier, load row blocks 0-3 and 4-7 (rows
   // 4b..4b+3) of the K, Q and V tiles; wave GW the g and beta rows.  In a
-  // partial chunk, rows past the end repeat row Ln - 1.
+  // partial chunk, rows past the end repeat row Ln - 1.  V is read by this
+  // work-group only, so it goes through L2 as non-temporal (as do the output
+  // rows): K and Q, which the other value head of the pair reads on the same
+  // XCD, and the parent states stay there longer.
   auto fetch = [&](int tc, int end, int buf) {
     // Offsets of once-per-chunk accesses are recomputed from an opaque copy
     // of the lane number rather than held in registers across the loop.
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
         const int lo = blk_off(blk);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sm.kb[buf] + lo), 16, ok, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sm.qb[buf] + lo), 16, ok, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sm.vb[buf] + lo), 16, ov, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sm.vb[buf] + lo), 16, ov, 0, 0, kCacheNT);
       }
     }
     if (cw == GW && lane < CH) {  // lane l writes LDS word l of the row
@@ -428,7 +431,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
     for (int bi = 0; bi < 4; ++bi) {
       const int orow = 4 * (4 * (cw - DW0) + bi) + (ln >> 4);
       const u32x4 v = *reinterpret_cast<const u32x4*>(sm.ost + orow * 256 + 16 * ((ln & 15) ^ (orow & 15)));
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, orow * rs_v + 16 * (ln & 15), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, orow * rs_v + 16 * (ln & 15), 0, kCacheNT);
     }
   };
 

@@ -109,6 +109,11 @@ bool scan_supported(int d_k, int d_v, int dtype);
 // forward when it reaches them.
 constexpr int kBwdCkpt = 8;
 
+// Cache-policy operand of the buffer load/store builtins on gfx950: bit 1 is
+// NT (non-temporal), which L2 keeps as the first line to evict.  For data a
+// work-group reads or writes exactly once.
+constexpr int kCacheNT = 2;
+
 struct ScanBwdArgs {
   const void* q;
   const void* k;

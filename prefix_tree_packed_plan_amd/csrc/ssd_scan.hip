@@ -301,10 +301,13 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_void*)(sm.ct[buf] + tile_blk(blk)), 16, ob, 0, 0, 0);
     }
     if (w < XB) {  // rows of 2P bytes, 1024 / (2P) rows per block
+      // x is read by this work-group alone: non-temporal (kCacheNT), so that
+      // it does not push out of L2 the B/C rows, dt and parent states that
+      // other heads of the segment read later.
       constexpr int RPB = 1024 / (2 * P), CPR = 2 * P / 16;
       const auto rx = rsrc(xg + (size_t(tc) * a.n_heads + h) * P, L * rs_x);
       const int ox = min(RPB * w + ln / CPR, Ln - 1) * rs_x + 16 * (ln % CPR);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sm.xt[buf] + 1024 * w), 16, ox, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sm.xt[buf] + 1024 * w), 16, ox, 0, 0, kCacheNT);
     }
     if (w == NW - 1 && lane < L) {
       const auto rd = rsrc(a.dt + size_t(tc) * a.n_heads + h, L * a.n_heads * 4);
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     for (int e = tid; e < L * CPR; e += 4 * P) {
       const int row = e / CPR, c = e % CPR;
       const u32x4 v = *reinterpret_cast<const u32x4*>(&sm.ys[buf][row * P + 8 * c]);
-      __builtin_amdgcn_raw_buffer_store_b128(v, ry, row * rs_x + 16 * c, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ry, row * rs_x + 16 * c, 0, kCacheNT);  // not read again here
     }
   };
 
