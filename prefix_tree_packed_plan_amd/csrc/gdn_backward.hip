@@ -606,10 +606,9 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
       }
       sm.gl[w][lh4] = glp;
     }
-    __syncthreads();  // U, dR staged
-
     // S0 rows 16w .. 16w+15 as the B operand of products with S0^T:
-    // S0row[jt][e] = S0[16w + i][16jt + 4h + e], from tile (w, jt).
+    // S0row[jt][e] = S0[16w + i][16jt + 4h + e], from tile (w, jt); issued
+    // before the barrier so that the round trip overlaps it.
     f32x4 S0row[NT];
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
@@ -617,6 +616,8 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) S0row[jt][e] = tp[4 * e];
     }
+    __syncthreads();  // U, dR staged
+
     {
       const f32x4 au = ld4(&sm.u[i16 * S + 16 * w + 4 * h4]);
       const f32x4 ar = ld4(&sm.r[i16 * S + 16 * w + 4 * h4]);
