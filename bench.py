@@ -61,18 +61,23 @@ def conv_bytes_per_token(s):
     return 2 * s.channels * e
 
 
-def kernel_source_hash():
+# Sources whose change invalidates a kernel's committed counter summary.
+FWD_SOURCES = ("gdn_scan.hip", "gdn_scan_d128.hip", "tree_conv.hip")
+SSD_SOURCES = ("ssd_scan.hip", "chunk_mfma.hpp")
+
+
+def kernel_source_hash(files=FWD_SOURCES):
     h = hashlib.sha256()
-    for f in ("gdn_scan.hip", "gdn_scan_d128.hip", "tree_conv.hip"):
+    for f in files:
         with open(os.path.join(ROOT, "prefix_tree_packed_plan_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
+def load_traffic(kernel, workload, files=FWD_SOURCES):
     """The committed counter summary of `kernel` on `workload` (bytes per
     launch, launches per step), or None when the summary is missing or the
-    kernels changed since."""
+    kernel's sources changed since."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -80,7 +85,7 @@ def load_traffic(kernel, workload):
     except (OSError, ValueError):
         return None
     entry = data.get(f"{kernel}:{workload}")
-    if not entry or entry.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("source_hash") != kernel_source_hash(files):
         return None
     return entry
 
@@ -410,10 +415,14 @@ def main():
         # token, plus one write and one read of each parent's state.
         per_tok = 2 * sh["n_heads"] * sh["head_dim"] * 2 + 2 * sh["n_groups"] * sh["d_state"] * 2 + sh["n_heads"] * 4
         sb = wl.n_tokens * per_tok + 2 * st["n_parents"] * sh["n_heads"] * sh["d_state"] * sh["head_dim"] * 4
+        sc = load_traffic("tree_ssd_scan", s.name, SSD_SOURCES)
+        st_b = None if sc is None else sc["bytes_per_launch"] * sc["launches"]
         ssd = {"tree_ssd_scan": {
             "ms": yms, "unique_tokens_per_s": wl.n_tokens / yms * 1e3, "bytes": sb, "GB/s": sb / yms / 1e6,
             "roofline": {"bound": "hbm", "achieved": sb / yms / 1e6, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": sb / (HBM_PEAK_GBS * 1e9) / (yms * 1e-3)},
+                         "frac": sb / (HBM_PEAK_GBS * 1e9) / (yms * 1e-3),
+                         "traffic_per_call": st_b,
+                         "traffic_over_algorithmic": None if st_b is None else st_b / sb},
             "shape": dict(sh, dtype="bf16"), "launches": st["n_levels"], "reps": reps}}
         del si, yb, ssws
 
