@@ -616,7 +616,10 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) S0row[jt][e] = tp[4 * e];
     }
-    __syncthreads();  // U, dR staged
+    // The partial products below read only this wave's own columns of U and
+    // dR, which it has just written: LDS serves one wave's accesses in order,
+    // so only the compiler has to be kept from reordering them.
+    asm volatile("" ::: "memory");
 
     {
       const f32x4 au = ld4(&sm.u[i16 * S + 16 * w + 4 * h4]);
