@@ -506,7 +506,17 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
   a.dq = grouped ? per_head : dq;
   a.dk = grouped ? per_head + static_cast<size_t>(n_tokens) * h_v * d_k : dk;
   a.dq_heads = grouped ? h_v : h_qk;
-  a.dq_accum = pairwise ? 1 : 0;
+  // Pairwise: the first value head of every pair stores its part of dq, dk
+  // and the second, in a later launch, adds to it (a + b either way round),
+  // so nothing needs clearing.  Level l's first heads run in the launch
+  // after level l + 1's first heads, together with level l + 1's second.
+  a.dq_accum = 0;
+  a.dq_accum2 = 0;
+  a.head_step = 1;
+  a.head_off = 0;
+  a.head_off2 = 0;
+  a.items2 = nullptr;
+  a.n_items2 = 0;
   a.seg_off = base + p.m_seg_off;
   a.parent = base + p.m_parent;
   a.root_idx = base + p.m_root;
@@ -554,9 +564,21 @@ int tree_gdn_scan_backward(const void* q, const void* k, const void* v, const fl
     if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);
   }
   // Deepest level first: a parent sums its children's start-state gradients.
-  for (int32_t l = p.n_levels - 1; l >= 0; --l) {
-    a.items = base + p.m_order + p.level_start[l];
-    a.n_items = p.level_start[l + 1] - p.level_start[l];
+  for (int32_t l = p.n_levels - 1; l >= (pairwise ? -1 : 0); --l) {
+    const int32_t ld = l + 1;  // the level below, whose second heads run now
+    a.items = l >= 0 ? base + p.m_order + p.level_start[l] : nullptr;
+    a.n_items = l >= 0 ? p.level_start[l + 1] - p.level_start[l] : 0;
+    a.head_step = pairwise ? 2 : 1;
+    a.head_off = 0;
+    a.dq_accum = 0;
+    a.items2 = nullptr;
+    a.n_items2 = 0;
+    if (pairwise && ld < p.n_levels) {
+      a.items2 = base + p.m_order + p.level_start[ld];
+      a.n_items2 = p.level_start[ld + 1] - p.level_start[ld];
+      a.head_off2 = 1;
+      a.dq_accum2 = 1;
+    }
     const hipError_t e = tg::launch_scan_backward_level(a, d_k, dtype, st);
     if (e != hipSuccess) return hip_fail("tree_gdn_scan_backward: launch", e);
   }

@@ -35,14 +35,16 @@
 // (I + N)(I + N^2)(I + N^4)(I + N^8), N = -A: six 16x16 MFMA products.
 //
 // Launches: a prep kernel computes every chunk's T, KK and QK (state-free, all
-// chunks at once) and clears dq, dk where parts are added; a checkpoint pass
-// re-runs every segment forward from its parent's final state (the forward's
-// `states`; all segments at once) and writes the start state of every
-// kBwdCkpt-th chunk to the workspace (the states kernel below; at bf16 d =
-// 128 the forward scan kernel's own checkpoint instantiation, which also
-// writes the chunk tables, so that prep only clears); then one launch per
-// trie level, deepest first, walks each segment's chunks backwards,
-// re-running the chunks between two checkpoints forward when it reaches them.  Work
+// chunks at once); a checkpoint pass re-runs every segment forward from its
+// parent's final state (the forward's `states`; all segments at once) and
+// writes the start state of every kBwdCkpt-th chunk to the workspace (the
+// states kernel below; at bf16 d = 128 the forward scan kernel's own
+// checkpoint instantiation, which also writes the chunk tables, in place of
+// prep); then launches level by level, deepest first, walk each segment's
+// chunks backwards, re-running the chunks between two checkpoints forward
+// when they reach them.  With two value heads per q/k head, the first head of
+// each pair stores its part of dq and dk and the second, one launch later,
+// adds to it (see the level loop of tree_gdn_scan_backward).  Work
 // item: one segment and one value head per work-group of d/16 waves; wave w
 // owns column tile w (16 columns) of every [16, d] chunk tensor and of the
 // state gradient dS, which stays in MFMA accumulator registers across the
@@ -311,9 +313,15 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
   const int i16 = lane & 15;
   const int col = 16 * w + i16;
 
-  const int item = blockIdx.x / a.h_v;
-  const int h = blockIdx.x - item * a.h_v;
-  const int seg = a.items[item];
+  // This launch's work items: group 0, then group 1 (see ScanBwdArgs).
+  const int hv_n = a.h_v / a.head_step;
+  const int g0 = a.n_items * hv_n;
+  const bool grp1 = int(blockIdx.x) >= g0;
+  const int bl = grp1 ? int(blockIdx.x) - g0 : int(blockIdx.x);
+  const int item = bl / hv_n;
+  const int h = (bl - item * hv_n) * a.head_step + (grp1 ? a.head_off2 : a.head_off);
+  const bool dq_add = grp1 ? a.dq_accum2 : a.dq_accum;
+  const int seg = (grp1 ? a.items2 : a.items)[item];
   const int hq = h / (a.h_v / a.h_qk);
   const int t_beg = a.seg_off[seg], t_end = a.seg_off[seg + 1];
   const int nc = (t_end - t_beg + L - 1) / L;
@@ -711,15 +719,15 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
     dK = mm(dKKt, kc, dK);
     dK = mm(dKK, kc, dK);
     dK = dK + xu - gt.gam * xv;
-    // With two value heads per q/k head, each adds its part into the zeroed
-    // dq, dk: 0 + a + b rounds the same in either order, so the sum is
-    // deterministic and equal to the ordered head-group sum.
+    // With two value heads per q/k head, the first stores its part of dq, dk
+    // and the second, in a later launch, adds to it: a + b, deterministic and
+    // equal to the ordered head-group sum.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * h4 + r;
       if (row < n) {
         const size_t o = (size_t(t0 + row) * a.dq_heads + dq_head) * D + col;
-        if (a.dq_accum) {
+        if (dq_add) {
           unsafeAtomicAdd(a.dq + o, dQ[r]);
           unsafeAtomicAdd(a.dk + o, dK[r]);
         } else {
@@ -803,9 +811,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_kernel(ScanBwdArgs a) {
 // all chunks of the trie run in parallel before the level launches.  One
 // wave per (chunk, value head); tokens past a segment's end are zero rows
 // with g = beta = 0, as in the level kernel.
-// TABLES = false: only the clearing of dq, dk below (the tables come from the
-// forward kernel's checkpoint pass).
-template <int D, bool F32IN, bool TABLES>
+template <int D, bool F32IN>
 __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(ScanBwdArgs a) {
   __shared__ float sg[4][L], sb[4][L];
   const int lane = threadIdx.x & 63;
@@ -820,66 +826,44 @@ __global__ __launch_bounds__(256) void gdn_bwd_prep_kernel(ScanBwdArgs a) {
   const int hq = h / (a.h_v / a.h_qk);
   const int t0 = a.seg_off[seg] + (c - a.gchunk[seg]) * L;
   const int n = live ? min(L, a.seg_off[seg + 1] - t0) : 0;
-  if constexpr (TABLES) {
-    if (lane < L) {
-      const bool tin = lane < n;
-      sg[w][lane] = tin ? a.g[size_t(t0 + lane) * a.h_v + h] : 0.f;
-      sb[w][lane] = tin ? a.beta[size_t(t0 + lane) * a.h_v + h] : 0.f;
+  if (lane < L) {
+    const bool tin = lane < n;
+    sg[w][lane] = tin ? a.g[size_t(t0 + lane) * a.h_v + h] : 0.f;
+    sb[w][lane] = tin ? a.beta[size_t(t0 + lane) * a.h_v + h] : 0.f;
+  }
+  const bool rin = i16 < n;
+  const size_t rbase = (size_t(t0 + (rin ? i16 : 0)) * a.h_qk + hq) * D;
+  f32x4 kk = z4(), qk = z4();
+  if constexpr (F32IN) {
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+      const f32x4 ak = rin ? load4<true>(a.k, rbase + 16 * m + 4 * h4) : z4();
+      const f32x4 aq = rin ? load4<true>(a.q, rbase + 16 * m + 4 * h4) : z4();
+      kk = mm(ak, ak, kk);
+      qk = mm(aq, ak, qk);
     }
-    const bool rin = i16 < n;
-    const size_t rbase = (size_t(t0 + (rin ? i16 : 0)) * a.h_qk + hq) * D;
-    f32x4 kk = z4(), qk = z4();
-    if constexpr (F32IN) {
+  } else {
 #pragma unroll
-      for (int m = 0; m < D / 16; ++m) {
-        const f32x4 ak = rin ? load4<true>(a.k, rbase + 16 * m + 4 * h4) : z4();
-        const f32x4 aq = rin ? load4<true>(a.q, rbase + 16 * m + 4 * h4) : z4();
-        kk = mm(ak, ak, kk);
-        qk = mm(aq, ak, qk);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < D / 32; ++m) {
-        const size_t i0 = rbase + 32 * m + 4 * h4;
-        const uint4 ak = rin ? cat(pack4(load4<false>(a.k, i0)), pack4(load4<false>(a.k, i0 + 16))) : make_uint4(0, 0, 0, 0);
-        const uint4 aq = rin ? cat(pack4(load4<false>(a.q, i0)), pack4(load4<false>(a.q, i0 + 16))) : make_uint4(0, 0, 0, 0);
-        kk = mma32(ak, ak, kk);  // bf16 x bf16 products are exact in fp32
-        qk = mma32(aq, ak, qk);
-      }
-    }
-    __syncthreads();
-    const Gates gt = make_gates(sg[w], sb[w], h4, i16);
-    f32x4 T, Tt;
-    solve(kk, gt, h4, i16, T, Tt);
-    if (live) {
-      float* tp = a.tws + (size_t(c) * a.h_v + h) * (3 * L * L);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = (4 * h4 + r) * L + i16;
-        tp[e] = T[r];
-        tp[L * L + e] = kk[r];
-        tp[2 * L * L + e] = qk[r];
-      }
+    for (int m = 0; m < D / 32; ++m) {
+      const size_t i0 = rbase + 32 * m + 4 * h4;
+      const uint4 ak = rin ? cat(pack4(load4<false>(a.k, i0)), pack4(load4<false>(a.k, i0 + 16))) : make_uint4(0, 0, 0, 0);
+      const uint4 aq = rin ? cat(pack4(load4<false>(a.q, i0)), pack4(load4<false>(a.q, i0 + 16))) : make_uint4(0, 0, 0, 0);
+      kk = mma32(ak, ak, kk);  // bf16 x bf16 products are exact in fp32
+      qk = mma32(aq, ak, qk);
     }
   }
-  if (!live) return;
-  // Two value heads per q/k head add into dq and dk in the level launches:
-  // the first of the pair clears the chunk's rows here, before them.
-  if (a.dq_accum && (h & 1) == 0) {
-    if (((reinterpret_cast<uintptr_t>(a.dq) | reinterpret_cast<uintptr_t>(a.dk)) & 15) == 0) {
-      // Whole rows in 16-byte pieces, non-temporal: the rows are next touched
-      // by the level launches, long after.
-      for (int e = lane; e < n * (D / 4); e += 64) {
-        const size_t o = (size_t(t0 + e / (D / 4)) * a.dq_heads + hq) * D + 4 * (e % (D / 4));
-        __builtin_nontemporal_store(z4(), reinterpret_cast<f32x4*>(a.dq + o));
-        __builtin_nontemporal_store(z4(), reinterpret_cast<f32x4*>(a.dk + o));
-      }
-    } else {
-      for (int e = lane; e < n * D; e += 64) {
-        const size_t o = (size_t(t0 + e / D) * a.dq_heads + hq) * D + (e % D);
-        a.dq[o] = 0.f;
-        a.dk[o] = 0.f;
-      }
+  __syncthreads();
+  const Gates gt = make_gates(sg[w], sb[w], h4, i16);
+  f32x4 T, Tt;
+  solve(kk, gt, h4, i16, T, Tt);
+  if (live) {
+    float* tp = a.tws + (size_t(c) * a.h_v + h) * (3 * L * L);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = (4 * h4 + r) * L + i16;
+      tp[e] = T[r];
+      tp[L * L + e] = kk[r];
+      tp[2 * L * L + e] = qk[r];
     }
   }
 }
@@ -900,8 +884,9 @@ __global__ void head_group_sum(const float* __restrict__ src, float* __restrict_
 
 template <int D, bool F32IN>
 hipError_t launch_bwd_level(const ScanBwdArgs& a, hipStream_t stream) {
-  if (a.n_items <= 0) return hipSuccess;
-  gdn_bwd_kernel<D, F32IN><<<dim3(a.n_items * a.h_v), dim3(4 * D), 0, stream>>>(a);
+  const int n = (a.n_items + a.n_items2) * (a.h_v / a.head_step);
+  if (n <= 0) return hipSuccess;
+  gdn_bwd_kernel<D, F32IN><<<dim3(n), dim3(4 * D), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -909,10 +894,7 @@ template <int D, bool F32IN>
 hipError_t launch_prep(const ScanBwdArgs& a, bool tables, bool states, hipStream_t stream) {
   const int64_t items = int64_t(a.n_chunks) * a.h_v;
   if (items <= 0) return hipSuccess;
-  if (tables)
-    gdn_bwd_prep_kernel<D, F32IN, true><<<dim3(unsigned((items + 3) / 4)), dim3(256), 0, stream>>>(a);
-  else
-    gdn_bwd_prep_kernel<D, F32IN, false><<<dim3(unsigned((items + 3) / 4)), dim3(256), 0, stream>>>(a);
+  if (tables) gdn_bwd_prep_kernel<D, F32IN><<<dim3(unsigned((items + 3) / 4)), dim3(256), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !states) return e;
   gdn_bwd_states_kernel<D, F32IN><<<dim3(unsigned(a.n_seg * a.h_v)), dim3(4 * D), 0, stream>>>(a);

@@ -146,21 +146,28 @@ struct ScanBwdArgs {
   const int32_t* gck;    // first checkpoint slot of each segment
   int32_t n_chunks;      // total chunks (prep launch)
   int32_t n_seg;         // segments (states launch)
-  const int32_t* items;  // segments of this level
+  // A level launch runs two groups of work items: value heads head_off,
+  // head_off + head_step, ... of the n_items segments at items (group 0),
+  // then those from head_off2 of the n_items2 segments at items2 (group 1).
+  // A group with dq_accum set adds its part of dq, dk instead of storing it.
+  const int32_t* items;
   int32_t n_items;
+  const int32_t* items2;
+  int32_t n_items2;
+  int32_t head_step;
+  int32_t head_off, head_off2;
+  int32_t dq_accum, dq_accum2;
   int32_t h_qk;
   int32_t h_v;
   int32_t dq_heads;      // h_qk (dq, dk written per q/k head) or h_v (per value head)
-  int32_t dq_accum;      // 1: two value heads per q/k head add into dq, dk (dq_heads = h_qk), cleared by prep
   float scale;
 };
 
 // Scan backward (gdn_backward.hip); d = d_k = d_v.  The prep launches compute
-// every chunk's T, KK and QK (state-free) and every chunk's start state;
-// then one launch per trie level.
-// Prep (T, KK, QK of every chunk, unless `tables` is false; dq, dk cleared
-// where parts are added) and, with `states`, the checkpoint pass of the
-// states kernel.
+// every chunk's T, KK and QK (state-free) and the checkpoint start states;
+// then the level launches, deepest level first.
+// Prep (T, KK, QK of every chunk, when `tables`) and, with `states`, the
+// checkpoint pass of the states kernel.
 hipError_t launch_scan_backward_prep(const ScanBwdArgs& a, int d, int dtype, bool tables, bool states,
                                      hipStream_t stream);
 hipError_t launch_scan_backward_level(const ScanBwdArgs& a, int d, int dtype, hipStream_t stream);
