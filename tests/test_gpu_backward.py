@@ -140,6 +140,37 @@ def test_scan_backward_matches_the_oracle(dtype, d, heads):
     assert max(errs.values()) <= SCAN_GRAD_RTOL, errs
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 128)])
+@pytest.mark.parametrize("shape", ["roots_only", "deep_chain"])
+def test_scan_backward_paired_heads_level_launches(dtype, d, shape):
+    """Two value heads per q/k head: the first head of each pair stores its
+    part of dq and dk and the second adds to it one launch later, with level
+    l's first heads sharing a launch with level l + 1's second heads.  The
+    end cases of that schedule: a forest of roots only (one level: the first
+    heads, then the second heads alone) and a chain of six levels."""
+    from oracle import grad as ograd
+    ptp = __import__("prefix_tree_packed_plan_amd")
+    if shape == "roots_only":
+        parents = np.array([-1, -1, -1], np.int32)
+        lens = np.array([5, 16, 40], np.int32)
+    else:
+        parents = np.array([-1, 0, 1, 2, 3, 4], np.int32)
+        lens = np.array([17, 3, 16, 1, 20, 9], np.int32)
+    n = int(lens.sum())
+    say(f"scan backward paired heads {shape} dtype={dtype} d={d} N={n}")
+    t = make_scan_inputs(n, 2, 4, d, d, dtype, DEV, seed=41)
+    do = make_scan_inputs(n, 2, 4, d, d, dtype, DEV, seed=42)["v"]
+    plan = ptp.tree_plan(parents, lens, 4)
+    got = _scan_grads(ptp, plan, t, do, 0.8)
+    torch.cuda.synchronize()
+    f = parity.to_np
+    ref = ograd.tree_gdn_vjp(parents, lens, f(t["q"]), f(t["k"]), f(t["v"]), f(t["g"]), f(t["beta"]), f(do),
+                             scale=0.8)
+    errs = {nm: rel(f(a), b) for nm, a, b in zip(GRAD_NAMES, got, ref)}
+    say("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert max(errs.values()) <= SCAN_GRAD_RTOL, errs
+
+
 def test_scan_backward_single_token_segments_and_zero_gradients():
     """Degenerate shapes: a chain of one-token segments under a root of one
     token, and a zero upstream gradient (every gradient exactly zero)."""
