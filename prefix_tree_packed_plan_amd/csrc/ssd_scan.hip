@@ -214,6 +214,21 @@ __global__ __launch_bounds__(4 * P, 2) void ssd_level_kernel(SsdArgs a) {
 // by transposing reads), the state's hi/lo split takes its residual from an
 // MFMA, and the outputs are staged as bf16 and stored as whole rows during the
 // next chunk.
+// The chunk's gate tables, made once per work-group by one wave during the
+// previous chunk: Gamma^T in the lanes' accumulator order, gamma, delta and dt
+// by token, gamma_last (double-buffered), and the making wave's prefix G.
+// Empty where each wave makes its own gates: the extra LDS would cost the
+// two-wave instantiation a work-group per CU.
+template <bool SHARED>
+struct SsdGateTables {
+  alignas(16) float gmt[2][4 * 64];
+  alignas(16) float grow[2][3][L];
+  alignas(16) float glast[2][4];
+  alignas(16) float gp[L];
+};
+template <>
+struct SsdGateTables<false> {};
+
 template <int P>
 struct SsdTileSmem {
   alignas(16) char bt[2][kTileRow16];  // B rows of the chunk
@@ -221,6 +236,7 @@ struct SsdTileSmem {
   alignas(16) char xt[2][L * P * 2];   // x rows (row-major, 2P bytes each)
   alignas(16) float dt[2][L];
   alignas(16) uint16_t ys[2][L * P];   // staged outputs (bf16, row-major)
+  SsdGateTables<(P / 16 >= 4)> gt;
 };
 
 template <int P>
@@ -229,6 +245,10 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   constexpr int NT = N / 16;  // row tiles of the state
   constexpr int NW = P / 16;  // waves
   constexpr int XB = L * P * 2 / 1024;  // 1 KB DMA blocks of the x tile
+  // With four waves or more, one wave per chunk (in turn) makes the chunk's
+  // gate tables for all of them, a chunk ahead; with two, each wave makes its
+  // own (the shared form costs that instantiation occupancy).
+  constexpr bool SHARED_GATES = NW >= 4;
   __shared__ SsdTileSmem<P> sm;
 
   const int tid = threadIdx.x;
@@ -256,12 +276,18 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   // Loop-constant LDS offsets: operand reads of row i16 at columns 32m + 4h4
   // (o2 = o + 32, opaque); transposing reads of B at columns 16rt and of x at
   // this wave's columns.
+  // With shared gates tile_off(i16, 32m + 4h4) = aoff + (64 m ^ 64 (i16 & 3))
+  // is recomputed at each chunk from an opaque copy rather than held in
+  // eight registers; the two-wave form holds them.
+  const int ak64 = 64 * (i16 & 3), aoff = tile_off(i16, 4 * h4) - ak64;
   int ao[NT / 2], ao2[NT / 2];
+  if constexpr (!SHARED_GATES) {
 #pragma unroll
-  for (int m = 0; m < NT / 2; ++m) {
-    ao[m] = tile_off(i16, 32 * m + 4 * h4);
-    ao2[m] = ao[m] + 32;
-    asm volatile("" : "+v"(ao2[m]));
+    for (int m = 0; m < NT / 2; ++m) {
+      ao[m] = tile_off(i16, 32 * m + 4 * h4);
+      ao2[m] = ao[m] + 32;
+      asm volatile("" : "+v"(ao2[m]));
+    }
   }
   // B^T rows 16rt.. at bo[rt / 2] + 32 (rt % 2): the swizzle keeps a 16-column
   // step inside a 32-column block a plain 32-byte step, but not across blocks.
@@ -287,7 +313,7 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   // Chunk at token tc (rows past the segment end repeat its last row; their
   // dt is taken as zero below) into buffer buf.  Wave w loads B and C row
   // blocks w, w + NW, ...; the first waves the x blocks; the last wave dt.
-  auto fetch = [&](int tc, int end, int buf) {
+  auto fetch = [&](int tc, int end, int buf, int gw) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int Ln = min(L, end - tc);
@@ -309,7 +335,7 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
       const int ox = min(RPB * w + ln / CPR, Ln - 1) * rs_x + 16 * (ln % CPR);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(sm.xt[buf] + 1024 * w), 16, ox, 0, 0, kCacheNT);
     }
-    if (w == NW - 1 && lane < L) {
+    if (w == (SHARED_GATES ? gw : NW - 1) && lane < L) {
       const auto rd = rsrc(a.dt + size_t(tc) * a.n_heads + h, L * a.n_heads * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)sm.dt[buf], 4, min(lane, Ln - 1) * a.n_heads * 4, 0,
                                                0, 0);
@@ -320,6 +346,38 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   // dropped.  (Plain stores through the generic output pointer made the
   // compiler wait for every outstanding load, the next chunk's DMA included,
   // before the following LDS reads.)
+  // Gate tables of the chunk in buffer buf (n tokens), by the wave that
+  // loaded its dt: G = prefix of g = dt A over the chunk (DPP scan over each
+  // row of 16 lanes); padding rows have dt = 0.
+  auto make_gate_tables = [&](int n, int buf) {
+    if constexpr (SHARED_GATES) {
+      const float dti = i16 < n ? sm.dt[buf][i16] : 0.f;
+      float G = dti * Ah;
+      G += dpp<0x111>(G);
+      G += dpp<0x112>(G);
+      G += dpp<0x114>(G);
+      G += dpp<0x118>(G);
+      // G of every token through LDS: written and read by this wave alone,
+      // whose LDS accesses are served in order.
+      if (h4 == 0) sm.gt.gp[i16] = G;
+      asm volatile("" ::: "memory");
+      const f32x4 Gr = ld4(&sm.gt.gp[4 * h4]);
+      const float glast = sm.gt.gp[L - 1] * kLog2e, gc = G * kLog2e;
+      f32x4 gm;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * h4 + r;
+        gm[r] = i16 >= row ? ex2(gc - Gr[r] * kLog2e) : 0.f;
+      }
+      *reinterpret_cast<f32x4*>(&sm.gt.gmt[buf][4 * lane]) = gm;
+      if (h4 == 0) {
+        sm.gt.grow[buf][0][i16] = ex2(gc);
+        sm.gt.grow[buf][1][i16] = ex2(glast - gc);
+        sm.gt.grow[buf][2][i16] = dti;
+        if (i16 == 0) sm.gt.glast[buf][0] = ex2(glast);
+      }
+    }
+  };
   auto store_y = [&](int tc, int n, int buf) {
     constexpr int CPR = 2 * P / 16;  // 16-byte chunks per row
     const auto ry = rsrc(yg + (size_t(tc) * a.n_heads + h) * P, (n - 1) * rs_x + 2 * P);
@@ -331,7 +389,11 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   };
 
   const int t_beg = a.seg_off[seg], t_end = a.seg_off[seg + 1];
-  fetch(t_beg, t_end, 0);
+  fetch(t_beg, t_end, 0, 0);
+  if (SHARED_GATES && w == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's dt of the first chunk has landed
+    make_gate_tables(min(L, t_end - t_beg), 0);
+  }
   int s = 0, prev_t0 = -1, prev_n = 0;
   for (int t0 = t_beg;;) {
     const int n = min(L, t_end - t0);
@@ -348,18 +410,32 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     uint2 bT[NT];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) bT[rt] = tile_tr(Bs, bo[rt >> 1] + 32 * (rt & 1));
-    if (more) fetch(nt0, t_end, s ^ 1);
+    // The next chunk's gate tables: made by wave (chunk index + 1) % NW, which
+    // also loads that chunk's dt, at the end of this chunk.
+    const int gw = ((t0 - t_beg) / L + 1) % NW;
+    if (more) fetch(nt0, t_end, s ^ 1, gw);
     if (prev_t0 >= 0) store_y(prev_t0, prev_n, s ^ 1);
 
     // -- C B^T (exact), C S0 (S0 as hi + lo)
     f32x4 qkt = z4(), cs = z4();
+    int ab0 = aoff, ak = ak64;
+    if constexpr (SHARED_GATES) asm volatile("" : "+v"(ab0), "+v"(ak));
 #pragma unroll
     for (int m = 0; m < NT / 2; ++m) {
-      const uint4 ac = tile_a8(Cs, ao[m], ao2[m]);
+      int aom, ao2m;
+      if constexpr (SHARED_GATES) {
+        aom = ab0 + ((64 * m) ^ ak);
+        ao2m = aom + 32;
+        asm volatile("" : "+v"(ao2m));
+      } else {
+        aom = ao[m];
+        ao2m = ao2[m];
+      }
+      const uint4 ac = tile_a8(Cs, aom, ao2m);
       // Kept apart from the C read at the same offsets: fused into one
       // ds_read2st64_b64 they cost several times as much.
       asm volatile("" ::: "memory");
-      const uint4 ab = tile_a8(Bs, ao[m], ao2[m]);
+      const uint4 ab = tile_a8(Bs, aom, ao2m);
       qkt = mma32(ab, ac, qkt);
       uint4 sh, sl;
       split8m(St[2 * m], St[2 * m + 1], negI, sh, sl);
@@ -369,7 +445,13 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
     // -- gates: G = prefix of g = dt A over the chunk (DPP scan over each row
     //    of 16 lanes); padding rows have dt = 0
     Gates gt;
-    {
+    if constexpr (SHARED_GATES) {
+      gt.Gmt = ld4(&sm.gt.gmt[s][4 * lane]);
+      gt.gam = ld4(&sm.gt.grow[s][0][4 * h4]);
+      gt.del = ld4(&sm.gt.grow[s][1][4 * h4]);
+      gt.bet = ld4(&sm.gt.grow[s][2][4 * h4]);
+      gt.gam_last = sm.gt.glast[s][0];
+    } else {  // G = prefix of g = dt A over the chunk; padding rows have dt = 0
       const float dti = i16 < n ? sm.dt[s][i16] : 0.f;
       float G = dti * Ah;
       G += dpp<0x111>(G);
@@ -417,6 +499,10 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       St[rt] = mma16b(bT[rt], ul, mma16b(bT[rt], uh, gt.gam_last * St[rt]));
+    }
+    if (SHARED_GATES && more && w == gw) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of the next chunk have landed
+      make_gate_tables(min(L, t_end - nt0), s ^ 1);
     }
     prev_t0 = t0;
     prev_n = n;
