@@ -516,10 +516,16 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
   float* dst = a.states ? a.states + (size_t(seg) * a.n_heads + h) * hs
                         : (a.slot[seg] >= 0 ? a.slots + (size_t(a.slot[seg]) * a.n_heads + h) * hs : nullptr);
   if (dst) {
+    // Offsets from an opaque copy of the lane number: shared with the
+    // parent-state load at the top, they were held (spilled) across the
+    // whole segment.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int o = (4 * (ln >> 4)) * P + 16 * w + (ln & 15);
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[size_t(16 * rt + 4 * h4 + r) * P + col] = St[rt][r];
+      for (int r = 0; r < 4; ++r) dst[size_t(16 * rt + r) * P + o] = St[rt][r];
   }
 }
 
