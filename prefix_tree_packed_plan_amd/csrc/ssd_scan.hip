@@ -312,7 +312,9 @@ __global__ __launch_bounds__(4 * P) __attribute__((amdgpu_waves_per_eu(4, 4))) v
 
   // Chunk at token tc (rows past the segment end repeat its last row; their
   // dt is taken as zero below) into buffer buf.  Wave w loads B and C row
-  // blocks w, w + NW, ...; the first waves the x blocks; the last wave dt.
+  // blocks w, w + NW, ...; the first waves the x blocks; dt is loaded by wave
+  // gw, the one that makes the chunk's gate tables (with shared gates), else
+  // by the last wave.
   auto fetch = [&](int tc, int end, int buf, int gw) {
     int ln = lane;
     asm volatile("" : "+v"(ln));
