@@ -396,8 +396,8 @@ size_t tree_gdn_scan_backward_workspace_bytes(const tree_plan_t* plan, int32_t h
  *         forward wrote (tree_gdn_scan's `states`)    (read)
  * dq, dk  device, [n_tokens, h_qk, d_k] fp32 (summed over the value heads
  *         of each query/key head, in head order; with two value heads
- *         per q/k head both add into the zeroed output, which rounds the
- *         same in either order)                       (written)
+ *         per q/k head the first stores its part and the second adds to
+ *         it, which rounds as the ordered sum)        (written)
  * dv      device, [n_tokens, h_v, d_v] fp32           (written)
  * dg, dbeta device, [n_tokens, h_v] fp32              (written)
  * dinit_states device, [n_roots, h_v, d_k, d_v] fp32, or NULL (written)
